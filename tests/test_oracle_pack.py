@@ -1,0 +1,89 @@
+"""Pins for the oracle's 2-bit packing (CPU only)."""
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _table():
+    """Code table of the model card: bit pattern -> ternary value."""
+    t = {}
+    with open(os.path.join(GOLDEN, "halo_code_table.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#") or line.startswith("codes_per_byte"):
+                continue
+            bits, val = line.split()
+            t[int(bits, 2)] = int(val)
+    return t
+
+
+def _kv(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()
+                out[k] = int(v)
+    return out
+
+
+def test_golden_code_table_bytes():
+    table = _table()
+    enc = {v: b for b, v in table.items()}
+    assert set(enc) == {-1, 0, 1}
+    rng = np.random.default_rng(3)
+    codes = rng.integers(-1, 2, size=(5, 32)).astype(np.int8)
+    packed = oracle.pack_codes(codes)
+    assert packed.shape == (5, 8)
+    # Expected bytes built from the card's table with the bit-order reading:
+    # column 4b+r of a row in bits [2r, 2r+1] of byte b.
+    for i in range(5):
+        for b in range(8):
+            want = sum(enc[int(codes[i, 4 * b + r])] << (2 * r) for r in range(4))
+            assert packed[i, b] == want
+    # a few literal bytes
+    lit = np.array([[0, 1, -1, 0, 1, 1, 1, 1, -1, -1, -1, -1, -1, 0, 0, 1]], dtype=np.int8)
+    assert oracle.pack_codes(lit).tolist() == [[0x24, 0x55, 0xAA, 0x42]]
+
+
+def test_round_trip_and_no_unused_field():
+    rng = np.random.default_rng(4)
+    codes = rng.integers(-1, 2, size=(64, 256)).astype(np.int8)
+    packed = oracle.pack_codes(codes)
+    assert (oracle.unpack_codes(packed, 256) == codes).all()
+    fields = np.stack([(packed >> (2 * r)) & 3 for r in range(4)])
+    assert not (fields == 3).any()
+
+
+def test_unused_field_decodes_to_zero():
+    packed = np.array([[0xFF, 0x37]], dtype=np.uint8)  # 11 11 11 11 / 00 11 01 11
+    codes = oracle.unpack_codes(packed, 8)
+    assert codes.tolist() == [[0, 0, 0, 0, 0, 1, 0, 0]]
+
+
+def test_packed_size_matches_model_card():
+    """rows*cols/4 bytes per linear plus a bf16 scale per row, with bf16
+    embeddings and norms, gives the card's 346 MB packed file; the tensor
+    bytes of the raw state dict come within 1 MiB of its 943 MB."""
+    s = _kv("halo_sizes.txt")
+    d, f, kv, L, V = s["d_model"], s["d_ffn"], s["kv_width"], s["n_layers"], s["vocab"]
+    linears = [(d, d), (kv, d), (kv, d), (d, d), (f, d), (f, d), (d, f)]
+    # the byte count the packer produces for one small matrix of each width
+    for rows, cols in [(8, d), (8, f)]:
+        c = np.zeros((rows, cols), dtype=np.int8)
+        assert oracle.pack_codes(c).nbytes == rows * cols // 4
+    n_w = L * sum(r * c for r, c in linears)
+    n_rows = L * sum(r for r, _ in linears)
+    norms = (2 * L + 1) * d
+    emb = V * d
+    packed = n_w // 4 + 2 * n_rows + 2 * (emb + norms)
+    raw = 2 * (n_w + emb + norms)
+    MiB = float(1 << 20)
+    assert round(packed / MiB) == s["packed_MB"]
+    # the raw pickle carries some framing beyond the tensor bytes (942.2 MiB)
+    assert s["state_dict_bf16_MB"] - 1 < raw / MiB <= s["state_dict_bf16_MB"]
