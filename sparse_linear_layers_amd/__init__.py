@@ -1,0 +1,306 @@
+"""Sparse-BitLinear forward path on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libsbl.so`` (C ABI in ``include/sbl.h``).  Every
+function here only marshals arguments: it checks tensor dtypes and devices,
+allocates outputs with torch on the input's device, passes raw device
+pointers and torch's current HIP stream, and raises ``SblError`` on a non-zero
+status.  Every step of the computation runs in the HIP kernels of libsbl;
+there is no CPU or PyTorch fallback, and importing a function when the
+library is missing raises.
+
+Function names match the C entry points.  Tensors are torch.Tensors on a
+ROCm device:
+  W float32 [rows, cols]; x bfloat16 [tokens, cols]; masks uint8 bits;
+  packed uint8 [rows, cols/4]; scales float32 [rows] and bf16 bits (uint16
+  stored in int16 tensors, or torch.bfloat16 tensors).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "SblError", "lib_path", "load", "nm_mask_create", "ternary_quant_pack",
+    "nm_mask_quant_pack", "nm_mask_quant_pack_grouped", "act_quant_i8",
+    "sparse_bitlinear_gemm", "sparse24_bytes", "sparse24_compress",
+    "sparse_bitlinear_gemm_sparse24", "sparse_bitlinear_gemv",
+    "sparse_bitlinear_gemv_grouped", "GemvDesc", "RefreshDesc",
+    "SCALE_FROM_MASKED", "SCALE_F32", "SCALE_BF16", "GEMV_MAX_TOKENS",
+]
+
+SCALE_FROM_MASKED = 1
+SCALE_F32 = 0
+SCALE_BF16 = 1
+GEMV_MAX_TOKENS = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "libsbl.so")
+_lib = None
+
+
+class SblError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+class RefreshDesc(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("mask_bits", ctypes.c_void_p),
+                ("packed", ctypes.c_void_p), ("row_scale", ctypes.c_void_p),
+                ("row_scale_bf16", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64)]
+
+
+class GemvDesc(ctypes.Structure):
+    _fields_ = [("xq", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("packed", ctypes.c_void_p), ("row_scale", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("scale_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def load() -> ctypes.CDLL:
+    """Load libsbl.so (built in-tree by ``sparse_linear_layers_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        raise RuntimeError(
+            f"{_LIB} is not built; run `python -m sparse_linear_layers_amd.build` "
+            "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(_LIB)
+    P, I64, I, U = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
+    sig = {
+        "nm_mask_create": [P, I64, I64, I, I, P, P],
+        "ternary_quant_pack": [P, P, I64, I64, U, P, P, P, P],
+        "nm_mask_quant_pack": [P, I64, I64, I, I, U, P, P, P, P, P],
+        "nm_mask_quant_pack_grouped": [P, P, I, I, I, U, P],
+        "act_quant_i8": [P, I64, I64, P, P, P],
+        "sparse_bitlinear_gemm": [P, P, P, P, I, I64, I64, I64, P, P, P],
+        "sparse24_compress": [P, I64, I64, P, P, P],
+        "sparse_bitlinear_gemm_sparse24": [P, P, P, P, I, I64, I64, I64, P, P, P],
+        "sparse_bitlinear_gemv": [P, P, P, P, I, I64, I64, I64, P, P],
+        "sparse_bitlinear_gemv_grouped": [P, P, I, I64, P],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.sparse24_bytes.argtypes = [I64, I64]
+    lib.sparse24_bytes.restype = ctypes.c_size_t
+    lib.sbl_status_str.argtypes = [I]
+    lib.sbl_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise SblError(fn, status, load().sbl_status_str(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must live on a ROCm device, got {t.device}")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+_BF16_BITS = (torch.bfloat16, torch.int16, torch.uint16) if hasattr(torch, "uint16") \
+    else (torch.bfloat16, torch.int16)
+
+
+def nm_mask_create(W: torch.Tensor, n: int, m: int, out: torch.Tensor | None = None):
+    _need(W, torch.float32, "W", 2)
+    rows, cols = W.shape
+    if out is None:
+        out = torch.empty(rows * cols // 8, dtype=torch.uint8, device=W.device)
+    _check("nm_mask_create", load().nm_mask_create(_ptr(W), rows, cols, n, m, _ptr(out),
+                                                   _stream(W.device)))
+    return out
+
+
+def ternary_quant_pack(W: torch.Tensor, mask_bits: torch.Tensor | None = None,
+                       flags: int = 0, want_bf16: bool = True):
+    """-> (packed uint8 [rows, cols/4], scale float32 [rows], scale_bf16 int16 bits or None)."""
+    _need(W, torch.float32, "W", 2)
+    if mask_bits is not None:
+        _need(mask_bits, torch.uint8, "mask_bits")
+    rows, cols = W.shape
+    dev = W.device
+    packed = torch.empty((rows, cols // 4), dtype=torch.uint8, device=dev)
+    scale = torch.empty(rows, dtype=torch.float32, device=dev)
+    sb = torch.empty(rows, dtype=torch.int16, device=dev) if want_bf16 else None
+    _check("ternary_quant_pack", load().ternary_quant_pack(
+        _ptr(W), _ptr(mask_bits), rows, cols, flags, _ptr(packed), _ptr(scale), _ptr(sb),
+        _stream(dev)))
+    return packed, scale, sb
+
+
+def nm_mask_quant_pack(W: torch.Tensor, n: int, m: int, flags: int = 0,
+                       want_mask: bool = True, want_bf16: bool = True):
+    """-> (mask bits or None, packed, scale, scale_bf16 or None)."""
+    _need(W, torch.float32, "W", 2)
+    rows, cols = W.shape
+    dev = W.device
+    mask = torch.empty(rows * cols // 8, dtype=torch.uint8, device=dev) if want_mask else None
+    packed = torch.empty((rows, cols // 4), dtype=torch.uint8, device=dev)
+    scale = torch.empty(rows, dtype=torch.float32, device=dev)
+    sb = torch.empty(rows, dtype=torch.int16, device=dev) if want_bf16 else None
+    _check("nm_mask_quant_pack", load().nm_mask_quant_pack(
+        _ptr(W), rows, cols, n, m, flags, _ptr(mask), _ptr(packed), _ptr(scale), _ptr(sb),
+        _stream(dev)))
+    return mask, packed, scale, sb
+
+
+def _desc_array(descs, cls, device):
+    n = len(descs)
+    host = (cls * n)(*descs)
+    raw = torch.frombuffer(bytearray(bytes(host)), dtype=torch.uint8)
+    dev = raw.to(device)  # synchronous host->device copy
+    return host, dev
+
+
+def nm_mask_quant_pack_grouped(jobs, n: int, m: int, flags: int = 0):
+    """jobs: list of dicts with W, packed, scale and optional mask, scale_bf16
+    tensors (all preallocated).  One launch over all of them."""
+    if not jobs:
+        return
+    dev = jobs[0]["W"].device
+    ds = []
+    for j in jobs:
+        W = _need(j["W"], torch.float32, "W", 2)
+        mask, sb = j.get("mask"), j.get("scale_bf16")
+        ds.append(RefreshDesc(W.data_ptr(), mask.data_ptr() if mask is not None else None,
+                              j["packed"].data_ptr(), j["scale"].data_ptr(),
+                              sb.data_ptr() if sb is not None else None,
+                              W.shape[0], W.shape[1]))
+    host, devbuf = _desc_array(ds, RefreshDesc, dev)
+    _check("nm_mask_quant_pack_grouped", load().nm_mask_quant_pack_grouped(
+        ctypes.cast(host, ctypes.c_void_p), _ptr(devbuf), len(ds), n, m, flags, _stream(dev)))
+    return devbuf  # keep alive until the stream passes the launch
+
+
+def act_quant_i8(x: torch.Tensor):
+    """x bfloat16 [tokens, cols] -> (xq int8 [tokens, cols], beta float32 [tokens])."""
+    _need(x, _BF16_BITS, "x", 2)
+    T, K = x.shape
+    xq = torch.empty((T, K), dtype=torch.int8, device=x.device)
+    beta = torch.empty(T, dtype=torch.float32, device=x.device)
+    _check("act_quant_i8", load().act_quant_i8(_ptr(x), T, K, _ptr(xq), _ptr(beta),
+                                               _stream(x.device)))
+    return xq, beta
+
+
+def _scale_dtype(scale):
+    if scale.dtype == torch.float32:
+        return SCALE_F32
+    if scale.dtype in _BF16_BITS:
+        return SCALE_BF16
+    raise TypeError(f"row scale: float32 or bf16 bits, got {scale.dtype}")
+
+
+def sparse_bitlinear_gemm(xq, beta, packed, scale, want_acc: bool = False,
+                          y: torch.Tensor | None = None):
+    """-> (y float32 [T, N], acc int32 [T, N] or None)."""
+    _need(xq, torch.int8, "xq", 2)
+    _need(beta, torch.float32, "beta", 1)
+    _need(packed, torch.uint8, "packed", 2)
+    _need(scale, None, "scale", 1)
+    T, K = xq.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError("packed must be [N, K/4]")
+    dev = xq.device
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    acc = torch.empty((T, N), dtype=torch.int32, device=dev) if want_acc else None
+    _check("sparse_bitlinear_gemm", load().sparse_bitlinear_gemm(
+        _ptr(xq), _ptr(beta), _ptr(packed), _ptr(scale), _scale_dtype(scale), T, K, N,
+        _ptr(y), _ptr(acc), _stream(dev)))
+    return y, acc
+
+
+def sparse24_bytes(N: int, K: int) -> int:
+    return int(load().sparse24_bytes(N, K))
+
+
+def sparse24_compress(packed: torch.Tensor, bad_groups: torch.Tensor | None = None):
+    """packed uint8 [N, K/4] (2:4 codes) -> private smfmac operand image."""
+    _need(packed, torch.uint8, "packed", 2)
+    N, K = packed.shape[0], packed.shape[1] * 4
+    out = torch.empty(max(sparse24_bytes(N, K), 16), dtype=torch.uint8, device=packed.device)
+    _check("sparse24_compress", load().sparse24_compress(
+        _ptr(packed), N, K, _ptr(out), _ptr(bad_groups), _stream(packed.device)))
+    return out
+
+
+def sparse_bitlinear_gemm_sparse24(xq, beta, sp24, N: int, scale, want_acc: bool = False,
+                                   y: torch.Tensor | None = None):
+    _need(xq, torch.int8, "xq", 2)
+    _need(beta, torch.float32, "beta", 1)
+    _need(sp24, torch.uint8, "sparse24")
+    _need(scale, None, "scale", 1)
+    T, K = xq.shape
+    dev = xq.device
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    acc = torch.empty((T, N), dtype=torch.int32, device=dev) if want_acc else None
+    _check("sparse_bitlinear_gemm_sparse24", load().sparse_bitlinear_gemm_sparse24(
+        _ptr(xq), _ptr(beta), _ptr(sp24), _ptr(scale), _scale_dtype(scale), T, K, N,
+        _ptr(y), _ptr(acc), _stream(dev)))
+    return y, acc
+
+
+def sparse_bitlinear_gemv(xq, beta, packed, scale, y: torch.Tensor | None = None):
+    _need(xq, torch.int8, "xq", 2)
+    _need(beta, torch.float32, "beta", 1)
+    _need(packed, torch.uint8, "packed", 2)
+    _need(scale, None, "scale", 1)
+    T, K = xq.shape
+    N = packed.shape[0]
+    dev = xq.device
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    _check("sparse_bitlinear_gemv", load().sparse_bitlinear_gemv(
+        _ptr(xq), _ptr(beta), _ptr(packed), _ptr(scale), _scale_dtype(scale), T, K, N,
+        _ptr(y), _stream(dev)))
+    return y
+
+
+def gemv_descs(jobs):
+    """Build (host array, device tensor) descriptors for
+    sparse_bitlinear_gemv_grouped from dicts with xq, beta, packed, scale, y."""
+    dev = jobs[0]["xq"].device
+    ds = []
+    for j in jobs:
+        xq, packed, scale = j["xq"], j["packed"], j["scale"]
+        ds.append(GemvDesc(xq.data_ptr(), j["beta"].data_ptr(), packed.data_ptr(),
+                           scale.data_ptr(), j["y"].data_ptr(), xq.shape[1], packed.shape[0],
+                           _scale_dtype(scale), 0))
+    return _desc_array(ds, GemvDesc, dev)
+
+
+def sparse_bitlinear_gemv_grouped(host, devbuf, count: int, T: int, device) -> None:
+    _check("sparse_bitlinear_gemv_grouped", load().sparse_bitlinear_gemv_grouped(
+        ctypes.cast(host, ctypes.c_void_p), _ptr(devbuf), count, T, _stream(device)))

@@ -1,0 +1,97 @@
+// Per-token absmax int8 activation quantisation (W1.58A8).
+// "Sparse-BitNet Guide", "Mathematical Formulation of Sparse-BitLinear",
+// step 4, and its module in "End-to-End Implementation": beta = max|x|
+// clamped below at 1e-5, x~ = Clip(Round(x * (127/beta)), -128, 127).
+//
+// One wave per token; the token row (bf16) stays in registers between the
+// absmax reduction and the quantisation, so x is read once (2 B/element in,
+// 1 B/element out).  The absmax is an integer max over the magnitude bits,
+// exact and order-free.
+#include "sbl_device.h"
+#include "sbl_launch.h"
+
+namespace sbl {
+
+template <int CPL>  // 8-element (16-byte) chunks per lane; 0 = long-row loop
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x,
+                                                        int64_t tokens, int64_t cols,
+                                                        int8_t* __restrict__ xq,
+                                                        float* __restrict__ beta) {
+  const int lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= tokens) return;
+  const int64_t nchunks = cols >> 3;
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * cols);
+  uint2* dst = reinterpret_cast<uint2*>(xq + t * cols);
+  auto chunk_max = [](const uint4& d, uint32_t m) {
+    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+    return m;
+  };
+  auto quant8 = [](const uint4& d, float s) {
+    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float f = __uint_as_float(h ? (w[i] & 0xffff0000u) : (w[i] << 16));
+        float q = rintf(f * s);
+        q = fminf(fmaxf(q, -128.f), 127.f);
+        const uint32_t b = (uint32_t)(int32_t)q & 0xffu;
+        out[i >> 1] |= b << (8 * (2 * (i & 1) + h));
+      }
+    }
+    return make_uint2(out[0], out[1]);
+  };
+  uint32_t m = 0;
+  if constexpr (CPL > 0) {
+    uint4 v[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int64_t idx = lane + (int64_t)kWave * c;
+      v[c] = idx < nchunks ? src[idx] : make_uint4(0u, 0u, 0u, 0u);
+      m = chunk_max(v[c], m);
+    }
+    m = wave_max(m);
+    const float b = fmaxf(__uint_as_float(m << 16), 1e-5f);
+    const float s = __fdiv_rn(127.0f, b);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int64_t idx = lane + (int64_t)kWave * c;
+      if (idx < nchunks) dst[idx] = quant8(v[c], s);
+    }
+    if (lane == 0) beta[t] = b;
+  } else {
+    for (int64_t base = 0; base < nchunks; base += kWave) {
+      const int64_t idx = base + lane;
+      if (idx < nchunks) m = chunk_max(src[idx], m);
+    }
+    m = wave_max(m);
+    const float b = fmaxf(__uint_as_float(m << 16), 1e-5f);
+    const float s = __fdiv_rn(127.0f, b);
+    for (int64_t base = 0; base < nchunks; base += kWave) {
+      const int64_t idx = base + lane;
+      if (idx < nchunks) dst[idx] = quant8(src[idx], s);
+    }
+    if (lane == 0) beta[t] = b;
+  }
+}
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t tokens, int64_t cols, int8_t* xq,
+                            float* beta, hipStream_t stream) {
+  const int64_t need = (cols / 8 + kWave - 1) / kWave;
+  const dim3 grid((unsigned)((tokens + 3) / 4)), block(256);
+#define SBL_AQ(C) hipLaunchKernelGGL(act_quant_kernel<C>, grid, block, 0, stream, x, tokens, cols, xq, beta)
+  if (need <= 1) SBL_AQ(1);
+  else if (need <= 2) SBL_AQ(2);
+  else if (need <= 4) SBL_AQ(4);
+  else if (need <= 8) SBL_AQ(8);
+  else if (need <= 16) SBL_AQ(16);
+  else SBL_AQ(0);
+#undef SBL_AQ
+  return hipGetLastError();
+}
+
+}  // namespace sbl

@@ -1,0 +1,41 @@
+// Host-side launchers of the gfx950 kernels (internal to libsbl).  Each
+// returns the hipError_t of its launch(es); argument validation happens in
+// api.hip before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "sbl.h"
+
+namespace sbl {
+
+// Descriptors per grouped launch (their block offsets travel in the kernel
+// argument block); longer lists are split into several launches.
+constexpr int kMaxGroupedRefresh = 256;
+constexpr int kMaxGroupedGemv = 256;
+
+hipError_t launch_nm_mask(const float* W, int64_t rows, int64_t cols, int n, int m,
+                          uint8_t* mask_bits, hipStream_t stream);
+hipError_t launch_quant_pack(const float* W, const uint8_t* mask_in, int64_t rows, int64_t cols,
+                             int n, int m, int fuse_mask, unsigned flags, uint8_t* mask_out,
+                             uint8_t* packed, float* scale, uint16_t* scale_bf16,
+                             hipStream_t stream);
+hipError_t launch_quant_pack_grouped(const sbl_refresh_desc* host, const sbl_refresh_desc* dev,
+                                     int count, int n, int m, unsigned flags, hipStream_t stream);
+hipError_t launch_act_quant(const uint16_t* x, int64_t tokens, int64_t cols, int8_t* xq,
+                            float* beta, hipStream_t stream);
+hipError_t launch_gemm(const int8_t* xq, const float* beta, const uint8_t* packed,
+                       const void* scale, int scale_bf16, int64_t T, int64_t K, int64_t N, float* y,
+                       int32_t* acc, hipStream_t stream);
+hipError_t launch_sparse24_compress(const uint8_t* packed, int64_t N, int64_t K, void* out,
+                                    int32_t* bad_groups, hipStream_t stream);
+hipError_t launch_gemm_sparse24(const int8_t* xq, const float* beta, const void* sp,
+                                const void* scale, int scale_bf16, int64_t T, int64_t K, int64_t N,
+                                float* y, int32_t* acc, hipStream_t stream);
+hipError_t launch_gemv(const sbl_gemv_desc* host, const sbl_gemv_desc* dev_or_null, int count,
+                       int64_t T, hipStream_t stream);
+
+}  // namespace sbl

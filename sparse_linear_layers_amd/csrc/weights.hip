@@ -1,0 +1,388 @@
+// Weight-side kernels: N:M magnitude mask, per-row absmean ternary
+// quantisation with 2-bit packing, and both fused in one pass.
+//
+// N:M mask: "Sparse-BitNet" README, "N:M Structured Sparsity"; "Sparse-BitNet
+// Guide", "Mathematical Formulation of Sparse-BitLinear", step 1.
+// Absmean ternary codes: model card "halo-sparse-bitnet-3:4-500m", "Recipe"
+// (per row) and "Packed vs raw" (2-bit layout); guide steps 2-3.
+//
+// All three are HBM-bound streams over fp32 W (4 B/weight in; 1/8 B mask,
+// 1/4 B codes out).  The row kernels keep a whole row in registers (one
+// wave per row, 128-bit loads, lane l owning 4-column chunks l, l+64, ...),
+// so W is read exactly once even though the scale must be known before any
+// code is decided.
+#include "sbl_device.h"
+#include "sbl_launch.h"
+
+namespace sbl {
+
+// ---------------------------------------------------------------------------
+// Mask only: a flat stream over groups of M (M = 4: one float4 per lane;
+// M = 8: two).  Bits of 32/M adjacent lanes are OR-ed into one dword store.
+// ---------------------------------------------------------------------------
+template <int M>
+__global__ __launch_bounds__(256) void nm_mask_kernel(const float* __restrict__ W,
+                                                      int64_t groups, int n,
+                                                      uint32_t* __restrict__ out) {
+  constexpr int kLanesPerWord = 32 / M;
+  const int lane = lane_id();
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t base = wave * kWave; base < groups; base += nwaves * kWave) {
+    const int64_t g = base + lane;
+    uint32_t bits = 0;
+    if (g < groups) {
+      const float4* p = reinterpret_cast<const float4*>(W) + g * (M / 4);
+      uint32_t key[M];
+#pragma unroll
+      for (int q = 0; q < M / 4; ++q) {
+        float4 v = p[q];
+        key[4 * q + 0] = abs_key(v.x);
+        key[4 * q + 1] = abs_key(v.y);
+        key[4 * q + 2] = abs_key(v.z);
+        key[4 * q + 3] = abs_key(v.w);
+      }
+      bits = keep_mask<M>(key, n);
+    }
+    uint32_t word = bits << (M * (lane % kLanesPerWord));
+#pragma unroll
+    for (int s = 1; s < kLanesPerWord; s <<= 1) word |= (uint32_t)shfl_xor((int)word, s);
+    if ((lane % kLanesPerWord) == 0 && g < groups) out[g / kLanesPerWord] = word;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row kernel: scale, codes, packing, and optionally the mask.
+//   MODE 0: mask read from mask_in (or none when mask_in is null)
+//   MODE 1: mask computed here, m = 4 (one chunk = one group)
+//   MODE 2: mask computed here, m = 8 (a group spans lanes 2i and 2i+1)
+// CPL = 4-column chunks per lane held in registers; cols <= 256 * CPL.
+// ---------------------------------------------------------------------------
+struct RowJob {
+  const float* W;
+  const uint8_t* mask_in;
+  uint8_t* mask_out;
+  uint8_t* packed;
+  float* scale;
+  uint16_t* scale_bf16;
+  int64_t rows;
+  int64_t cols;
+};
+
+template <int CPL, int MODE>
+__device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, int n,
+                                               bool from_masked) {
+  const int lane = lane_id();
+  const int64_t cols = job.cols;
+  const int64_t nchunks = cols >> 2;
+  const float4* src = reinterpret_cast<const float4*>(job.W + row * cols);
+  float4 v[CPL];
+  uint32_t keep[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int64_t idx = lane + (int64_t)kWave * c;
+    v[c] = idx < nchunks ? src[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // ---- mask ----
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int64_t idx = lane + (int64_t)kWave * c;
+    if constexpr (MODE == 0) {
+      if (job.mask_in && idx < nchunks) {
+        const int64_t bit = row * cols + 4 * idx;
+        keep[c] = (job.mask_in[bit >> 3] >> (bit & 7)) & 0xFu;
+      } else {
+        keep[c] = 0xFu;
+      }
+    } else if constexpr (MODE == 1) {
+      uint32_t key[4] = {abs_key(v[c].x), abs_key(v[c].y), abs_key(v[c].z), abs_key(v[c].w)};
+      keep[c] = keep_mask<4>(key, n);
+    } else {
+      uint32_t mine[4] = {abs_key(v[c].x), abs_key(v[c].y), abs_key(v[c].z), abs_key(v[c].w)};
+      uint32_t other[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) other[e] = (uint32_t)shfl_xor((int)mine[e], 1);
+      const bool low_half = (lane & 1) == 0;
+      uint32_t key[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[e] = low_half ? mine[e] : other[e];
+        key[4 + e] = low_half ? other[e] : mine[e];
+      }
+      const uint32_t k8 = keep_mask<8>(key, n);
+      keep[c] = low_half ? (k8 & 0xFu) : (k8 >> 4);
+    }
+  }
+  // ---- scale: sum of |w| in double, lane partials then a butterfly ----
+  double s = 0.0;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const float a[4] = {fabsf(v[c].x), fabsf(v[c].y), fabsf(v[c].z), fabsf(v[c].w)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (!from_masked || ((keep[c] >> e) & 1u)) s += (double)a[e];
+  }
+  s = wave_sum(s);
+  float g = (float)(s / (double)cols);
+  g = fmaxf(g, 1e-5f);
+  // Clip(Round(w/g), -1, 1) is +-1 exactly when |w| > g/2 (g/2 is exact for
+  // g >= 1e-5, and w/g rounded to float exceeds 1/2 iff |w| > g/2).
+  const float thr = g * 0.5f;
+  // ---- codes, packed 4 per byte; 4 lanes' bytes form one dword store ----
+  uint32_t* dst = reinterpret_cast<uint32_t*>(job.packed + row * (cols >> 2));
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int64_t idx = lane + (int64_t)kWave * c;
+    const float w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+    uint32_t byte = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t f = fabsf(w[e]) > thr ? (w[e] < 0.f ? 2u : 1u) : 0u;
+      f = ((keep[c] >> e) & 1u) ? f : 0u;
+      byte |= f << (2 * e);
+    }
+    uint32_t word = byte << (8 * (lane & 3));
+    word |= (uint32_t)shfl_xor((int)word, 1);
+    word |= (uint32_t)shfl_xor((int)word, 2);
+    if ((lane & 3) == 0 && idx < nchunks) dst[idx >> 2] = word;
+    if constexpr (MODE != 0) {
+      if (job.mask_out) {
+        uint32_t mw = keep[c] << (4 * (lane & 7));
+        mw |= (uint32_t)shfl_xor((int)mw, 1);
+        mw |= (uint32_t)shfl_xor((int)mw, 2);
+        mw |= (uint32_t)shfl_xor((int)mw, 4);
+        if ((lane & 7) == 0 && idx < nchunks)
+          reinterpret_cast<uint32_t*>(job.mask_out)[(row * cols + 4 * idx) >> 5] = mw;
+      }
+    }
+  }
+  if (lane == 0) {
+    job.scale[row] = g;
+    if (job.scale_bf16) job.scale_bf16[row] = f32_to_bf16_rne(g);
+  }
+}
+
+// Rows longer than 256*32 columns: two passes over the row (the second
+// read is expected to hit L2), same arithmetic.
+template <int MODE>
+__device__ void quant_pack_row_long(const RowJob& job, int64_t row, int n, bool from_masked) {
+  const int lane = lane_id();
+  const int64_t cols = job.cols;
+  const int64_t nchunks = cols >> 2;
+  const float4* src = reinterpret_cast<const float4*>(job.W + row * cols);
+  auto mask_of = [&](int64_t idx, const float4& x) -> uint32_t {
+    if constexpr (MODE == 0) {
+      if (!job.mask_in) return 0xFu;
+      const int64_t bit = row * cols + 4 * idx;
+      return (job.mask_in[bit >> 3] >> (bit & 7)) & 0xFu;
+    } else if constexpr (MODE == 1) {
+      uint32_t key[4] = {abs_key(x.x), abs_key(x.y), abs_key(x.z), abs_key(x.w)};
+      return keep_mask<4>(key, n);
+    } else {
+      uint32_t mine[4] = {abs_key(x.x), abs_key(x.y), abs_key(x.z), abs_key(x.w)};
+      uint32_t other[4];
+      for (int e = 0; e < 4; ++e) other[e] = (uint32_t)shfl_xor((int)mine[e], 1);
+      const bool low_half = (lane & 1) == 0;
+      uint32_t key[8];
+      for (int e = 0; e < 4; ++e) {
+        key[e] = low_half ? mine[e] : other[e];
+        key[4 + e] = low_half ? other[e] : mine[e];
+      }
+      const uint32_t k8 = keep_mask<8>(key, n);
+      return low_half ? (k8 & 0xFu) : (k8 >> 4);
+    }
+  };
+  double s = 0.0;
+  for (int64_t base = 0; base < nchunks; base += kWave) {  // nchunks % 16 == 0
+    const int64_t idx = base + lane;
+    float4 x = idx < nchunks ? src[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t k = mask_of(idx, x);
+    const float a[4] = {fabsf(x.x), fabsf(x.y), fabsf(x.z), fabsf(x.w)};
+    for (int e = 0; e < 4; ++e)
+      if (!from_masked || ((k >> e) & 1u)) s += (double)a[e];
+  }
+  s = wave_sum(s);
+  float g = fmaxf((float)(s / (double)cols), 1e-5f);
+  const float thr = g * 0.5f;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(job.packed + row * (cols >> 2));
+  for (int64_t base = 0; base < nchunks; base += kWave) {
+    const int64_t idx = base + lane;
+    float4 x = idx < nchunks ? src[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t k = mask_of(idx, x);
+    const float w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t byte = 0;
+    for (int e = 0; e < 4; ++e) {
+      uint32_t f = fabsf(w[e]) > thr ? (w[e] < 0.f ? 2u : 1u) : 0u;
+      f = ((k >> e) & 1u) ? f : 0u;
+      byte |= f << (2 * e);
+    }
+    uint32_t word = byte << (8 * (lane & 3));
+    word |= (uint32_t)shfl_xor((int)word, 1);
+    word |= (uint32_t)shfl_xor((int)word, 2);
+    if ((lane & 3) == 0 && idx < nchunks) dst[idx >> 2] = word;
+    if constexpr (MODE != 0) {
+      if (job.mask_out) {
+        uint32_t mw = k << (4 * (lane & 7));
+        mw |= (uint32_t)shfl_xor((int)mw, 1);
+        mw |= (uint32_t)shfl_xor((int)mw, 2);
+        mw |= (uint32_t)shfl_xor((int)mw, 4);
+        if ((lane & 7) == 0 && idx < nchunks)
+          reinterpret_cast<uint32_t*>(job.mask_out)[(row * cols + 4 * idx) >> 5] = mw;
+      }
+    }
+  }
+  if (lane == 0) {
+    job.scale[row] = g;
+    if (job.scale_bf16) job.scale_bf16[row] = f32_to_bf16_rne(g);
+  }
+}
+
+template <int CPL, int MODE>
+__device__ __forceinline__ void quant_pack_dispatch(const RowJob& job, int64_t row, int n,
+                                                    bool from_masked) {
+  if constexpr (CPL == 0)
+    quant_pack_row_long<MODE>(job, row, n, from_masked);
+  else
+    quant_pack_row<CPL, MODE>(job, row, n, from_masked);
+}
+
+constexpr int kRowsPerBlock = 4;  // one wave per row
+
+template <int CPL, int MODE>
+__global__ __launch_bounds__(256) void quant_pack_kernel(RowJob job, int n, int from_masked) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= job.rows) return;  // whole wave leaves; no block barrier below
+  quant_pack_dispatch<CPL, MODE>(job, row, n, from_masked != 0);
+}
+
+// Grouped: the row-blocks of all matrices laid end to end; block_start[d]
+// is the first block of descriptor d (kept in the kernel argument).
+struct GroupedRefreshArgs {
+  const sbl_refresh_desc* descs;
+  int count;
+  int block_start[kMaxGroupedRefresh + 1];
+};
+
+template <int CPL, int MODE>
+__global__ __launch_bounds__(256) void quant_pack_grouped_kernel(GroupedRefreshArgs args, int n,
+                                                                 int from_masked) {
+  const int b = blockIdx.x;
+  int lo = 0, hi = args.count - 1;  // last d with block_start[d] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (args.block_start[mid] <= b) lo = mid; else hi = mid - 1;
+  }
+  const sbl_refresh_desc d = args.descs[lo];
+  const int64_t row = (int64_t)(b - args.block_start[lo]) * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= d.rows) return;
+  RowJob job{d.W, nullptr, d.mask_bits, d.packed, d.row_scale, d.row_scale_bf16, d.rows, d.cols};
+  quant_pack_dispatch<CPL, MODE>(job, row, n, from_masked != 0);
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+static int chunks_per_lane(int64_t cols) {
+  const int64_t need = (cols / 4 + kWave - 1) / kWave;
+  if (need <= 1) return 1;
+  if (need <= 2) return 2;
+  if (need <= 4) return 4;
+  if (need <= 8) return 8;
+  if (need <= 16) return 16;
+  if (need <= 32) return 32;
+  return 0;  // long-row path
+}
+
+hipError_t launch_nm_mask(const float* W, int64_t rows, int64_t cols, int n, int m,
+                          uint8_t* mask_bits, hipStream_t stream) {
+  const int64_t groups = rows * cols / m;
+  const int64_t blocks = std::min<int64_t>((groups + 255) / 256, 256 * 32);
+  if (m == 4)
+    hipLaunchKernelGGL(nm_mask_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, W,
+                       groups, n, reinterpret_cast<uint32_t*>(mask_bits));
+  else
+    hipLaunchKernelGGL(nm_mask_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, W,
+                       groups, n, reinterpret_cast<uint32_t*>(mask_bits));
+  return hipGetLastError();
+}
+
+template <int MODE>
+static void launch_row(int cpl, dim3 grid, hipStream_t stream, const RowJob& job, int n,
+                       int from_masked) {
+  switch (cpl) {
+#define SBL_CASE(C)                                                                        \
+  case C:                                                                                  \
+    hipLaunchKernelGGL((quant_pack_kernel<C, MODE>), grid, dim3(256), 0, stream, job, n, \
+                       from_masked);                                                       \
+    break;
+    SBL_CASE(1) SBL_CASE(2) SBL_CASE(4) SBL_CASE(8) SBL_CASE(16) SBL_CASE(32) SBL_CASE(0)
+#undef SBL_CASE
+  }
+}
+
+hipError_t launch_quant_pack(const float* W, const uint8_t* mask_in, int64_t rows, int64_t cols,
+                             int n, int m, int fuse_mask, unsigned flags, uint8_t* mask_out,
+                             uint8_t* packed, float* scale, uint16_t* scale_bf16,
+                             hipStream_t stream) {
+  RowJob job{W, mask_in, mask_out, packed, scale, scale_bf16, rows, cols};
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const int cpl = chunks_per_lane(cols);
+  const int fm = (flags & SBL_SCALE_FROM_MASKED) ? 1 : 0;
+  if (!fuse_mask)
+    launch_row<0>(cpl, grid, stream, job, n, fm);
+  else if (m == 4)
+    launch_row<1>(cpl, grid, stream, job, n, fm);
+  else
+    launch_row<2>(cpl, grid, stream, job, n, fm);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static void launch_grouped(int cpl, dim3 grid, hipStream_t stream, const GroupedRefreshArgs& a,
+                           int n, int fm) {
+  switch (cpl) {
+#define SBL_CASE(C)                                                                              \
+  case C:                                                                                        \
+    hipLaunchKernelGGL((quant_pack_grouped_kernel<C, MODE>), grid, dim3(256), 0, stream, a, n, \
+                       fm);                                                                      \
+    break;
+    SBL_CASE(1) SBL_CASE(2) SBL_CASE(4) SBL_CASE(8) SBL_CASE(16) SBL_CASE(32) SBL_CASE(0)
+#undef SBL_CASE
+  }
+}
+
+hipError_t launch_quant_pack_grouped(const sbl_refresh_desc* host, const sbl_refresh_desc* dev,
+                                     int count, int n, int m, unsigned flags,
+                                     hipStream_t stream) {
+  // One launch per run of descriptors that fits the argument block; every
+  // descriptor of one launch uses the chunks-per-lane of its widest row.
+  for (int first = 0; first < count;) {
+    const int last = std::min(count, first + kMaxGroupedRefresh);
+    GroupedRefreshArgs a;
+    a.descs = dev + first;
+    a.count = last - first;
+    int64_t blocks = 0;
+    int64_t max_cols = 0;
+    for (int d = first; d < last; ++d) {
+      a.block_start[d - first] = (int)blocks;
+      blocks += (host[d].rows + kRowsPerBlock - 1) / kRowsPerBlock;
+      max_cols = std::max(max_cols, host[d].cols);
+    }
+    a.block_start[last - first] = (int)blocks;
+    if (blocks > 0) {
+      const int cpl = chunks_per_lane(max_cols);
+      const int fm = (flags & SBL_SCALE_FROM_MASKED) ? 1 : 0;
+      const dim3 grid((unsigned)blocks);
+      if (m == 4)
+        launch_grouped<1>(cpl, grid, stream, a, n, fm);
+      else
+        launch_grouped<2>(cpl, grid, stream, a, n, fm);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    first = last;
+  }
+  return hipSuccess;
+}
+
+}  // namespace sbl

@@ -1,0 +1,117 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+declared in include/sbl.h, and rejects bad arguments before touching HIP.
+The fake device pointers below are never dereferenced: validation returns
+first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_linear_layers_amd as sbl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sbl.h")
+
+OK, ARG, SHAPE, ALIGN, UNSUP = 0, -1, -2, -3, -4
+P = 0x10000          # aligned fake pointer
+MIS = 0x10004        # misaligned fake pointer
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sbl.lib_path()):
+        from sparse_linear_layers_amd import build
+        build.build()
+    return sbl.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in (OK, ARG, SHAPE, ALIGN, UNSUP, -5, 99):
+        assert lib.sbl_status_str(s)
+
+
+def test_mask_validation(lib):
+    f = lib.nm_mask_create
+    assert f(None, 4, 64, 2, 4, P, None) == ARG
+    assert f(P, -1, 64, 2, 4, P, None) == ARG
+    assert f(P, 4, 60, 2, 4, P, None) == SHAPE
+    assert f(P, 4, 0, 2, 4, P, None) == SHAPE
+    assert f(P, 4, 65536 + 64, 2, 4, P, None) == SHAPE
+    assert f(P, 4, 64, 2, 3, P, None) == UNSUP
+    assert f(P, 4, 64, 5, 4, P, None) == UNSUP
+    assert f(P, 4, 64, -1, 8, P, None) == UNSUP
+    assert f(MIS, 4, 64, 2, 4, P, None) == ALIGN
+    assert f(P, 4, 64, 2, 4, MIS, None) == ALIGN
+    assert f(P, 0, 64, 2, 4, P, None) == OK  # empty: nothing launched
+
+
+def test_quant_validation(lib):
+    f = lib.ternary_quant_pack
+    assert f(P, None, 4, 64, 0, None, P, None, None) == ARG
+    assert f(P, None, 4, 64, 1, P, P, None, None) == ARG       # from-masked needs a mask
+    assert f(P, None, 4, 64, 2, P, P, None, None) == UNSUP     # unknown flag
+    assert f(P, None, 4, 96, 0, P, P, None, None) == SHAPE
+    assert f(P, None, 4, 64, 0, P, P, MIS, None) == ALIGN
+    assert f(P, None, 0, 64, 0, P, P, None, None) == OK
+    g = lib.nm_mask_quant_pack
+    assert g(P, 4, 64, 2, 6, 0, None, P, P, None, None) == UNSUP
+    assert g(P, 4, 64, 2, 4, 0, MIS, P, P, None, None) == ALIGN
+    assert g(P, 0, 64, 6, 8, 1, None, P, P, None, None) == OK
+
+
+def test_product_validation(lib):
+    f = lib.sparse_bitlinear_gemm
+    assert f(P, P, P, P, 0, 8, 64, 8, None, None, None) == ARG
+    assert f(P, P, P, P, 2, 8, 64, 8, P, None, None) == UNSUP   # scale dtype
+    assert f(P, P, P, P, 0, 8, 100, 8, P, None, None) == SHAPE
+    assert f(P, P, P, P, 0, 8, 64, 8, P, MIS, None) == ALIGN
+    assert f(P, P, P, P, 0, 0, 64, 8, P, None, None) == OK
+    assert f(P, P, P, P, 0, 8, 64, 0, P, None, None) == OK
+    v = lib.sparse_bitlinear_gemv
+    assert v(P, P, P, P, 0, 0, 64, 8, P, None) == UNSUP
+    assert v(P, P, P, P, 0, 17, 64, 8, P, None) == UNSUP
+    assert v(P, P, P, P, 1, 1, 64, 0, P, None) == OK
+    s = lib.sparse_bitlinear_gemm_sparse24
+    assert s(P, P, None, P, 0, 8, 64, 8, P, None, None) == ARG
+    assert lib.sparse24_compress(P, 8, 64, P, MIS + 2, None) == ALIGN
+    assert lib.sparse24_compress(P, 0, 64, P, None, None) == OK
+    assert lib.sparse24_bytes(896, 4864) == 896 * 4864 // 4
+
+
+def test_grouped_validation(lib):
+    d = (sbl.GemvDesc * 2)(sbl.GemvDesc(P, P, P, P, P, 64, 8, 0, 0),
+                           sbl.GemvDesc(P, P, P, P, P, 96, 8, 0, 0))
+    hp = ctypes.cast(d, ctypes.c_void_p)
+    assert lib.sparse_bitlinear_gemv_grouped(hp, P, 2, 1, None) == SHAPE
+    assert lib.sparse_bitlinear_gemv_grouped(hp, P, 0, 1, None) == OK
+    assert lib.sparse_bitlinear_gemv_grouped(hp, None, 2, 1, None) == ARG
+    assert lib.sparse_bitlinear_gemv_grouped(hp, P, 1, 20, None) == UNSUP
+    r = (sbl.RefreshDesc * 1)(sbl.RefreshDesc(P, None, P, P, MIS, 4, 64))
+    assert lib.nm_mask_quant_pack_grouped(ctypes.cast(r, ctypes.c_void_p), P, 1, 3, 4, 0, None) == ALIGN
+    assert lib.nm_mask_quant_pack_grouped(ctypes.cast(r, ctypes.c_void_p), P, 1, 3, 5, 0, None) == UNSUP
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The HIP package must not import or load anything under oracle/."""
+    pkg = os.path.join(ROOT, "sparse_linear_layers_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in text and "liboracle" not in text, fn
+                assert "sbl_oracle" not in text, fn

@@ -1,0 +1,350 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Bit-exact for masks, packed codes, row scales (float and
+bf16), int8 activations, beta and int32 accumulators; y within 1e-6
+relative (three float roundings of an exact integer product are at most
+~1.8e-7 apart from the exactly rounded value)."""
+import numpy as np
+import pytest
+
+import oracle
+from brute import unpack_bits
+
+from sparse_linear_layers_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+Y_RTOL = 1e-6
+
+
+@pytest.fixture(scope="module")
+def sbl():
+    import sparse_linear_layers_amd as m
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.load()
+    return m
+
+
+DEV = "cuda:0"
+
+
+def dev(a):
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t, dtype=None):
+    a = t.cpu().numpy()
+    return a.view(dtype) if dtype is not None else a
+
+
+def assert_y_close(got, want):
+    got = got.astype(np.float64)
+    want = want.astype(np.float64)
+    nz = want != 0
+    assert (got[~nz] == 0).all()
+    rel = np.abs(got[nz] - want[nz]) / np.abs(want[nz])
+    assert rel.size == 0 or rel.max() <= Y_RTOL, rel.max()
+
+
+def tie_heavy(tag, rows, cols):
+    r = synth.rng(tag)
+    alphabet = np.array([0.0, -0.0, 0.01, -0.01, 0.02, -0.02, 0.03], dtype=np.float32)
+    return r.choice(alphabet, size=(rows, cols)).astype(np.float32)
+
+
+# --------------------------------------------------------------------- mask
+@pytest.mark.parametrize("n,m", [(3, 4), (2, 4), (1, 4), (4, 4), (0, 4), (2, 8), (4, 8), (6, 8)])
+@pytest.mark.parametrize("rows,cols", [(1, 64), (37, 256), (512, 896), (33, 4864)])
+def test_nm_mask(sbl, n, m, rows, cols):
+    W = synth.latent_weight(f"gpu/mask/{rows}x{cols}", rows, cols)
+    got = host(sbl.nm_mask_create(dev(W), n, m))
+    assert np.array_equal(got, oracle.nm_mask(W, n, m))
+
+
+@pytest.mark.parametrize("n,m", [(3, 4), (2, 4), (6, 8)])
+def test_nm_mask_ties(sbl, n, m):
+    W = tie_heavy("gpu/mask/ties", 64, 512)
+    got = host(sbl.nm_mask_create(dev(W), n, m))
+    assert np.array_equal(got, oracle.nm_mask(W, n, m))
+
+
+# ------------------------------------------------------------ quant + pack
+def _check_quant(W, mask, flags, packed, scale, sb):
+    from_masked = bool(flags & 1)
+    g_ref, gb_ref = oracle.row_scale(W, mask, from_masked)
+    g = host(scale)
+    # the decision given the device's scale is bit-exact
+    codes_given = oracle.ternary_codes(W, mask, g)
+    assert np.array_equal(host(packed), oracle.pack_codes(codes_given))
+    # and the scale itself equals the oracle's (both are the mean rounded
+    # once to float)
+    assert np.array_equal(g, g_ref)
+    if sb is not None:
+        assert np.array_equal(host(sb, np.uint16), gb_ref)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 64), (5, 256), (37, 896), (64, 4864), (9, 7168), (3, 9216)])
+@pytest.mark.parametrize("mode", ["dense", "mask", "mask_from_masked"])
+def test_ternary_quant_pack(sbl, rows, cols, mode):
+    W = synth.latent_weight(f"gpu/quant/{rows}x{cols}", rows, cols)
+    mask = None if mode == "dense" else oracle.nm_mask(W, 3, 4)
+    flags = 1 if mode == "mask_from_masked" else 0
+    packed, scale, sb = sbl.ternary_quant_pack(dev(W), None if mask is None else dev(mask), flags)
+    _check_quant(W, mask, flags, packed, scale, sb)
+
+
+@pytest.mark.parametrize("n,m", [(3, 4), (2, 4), (4, 8), (6, 8)])
+@pytest.mark.parametrize("rows,cols", [(1, 64), (21, 896), (16, 4864), (4, 9216)])
+@pytest.mark.parametrize("flags", [0, 1])
+def test_nm_mask_quant_pack_fused(sbl, n, m, rows, cols, flags):
+    W = synth.latent_weight(f"gpu/fused/{rows}x{cols}", rows, cols)
+    mask_d, packed, scale, sb = sbl.nm_mask_quant_pack(dev(W), n, m, flags)
+    mask = oracle.nm_mask(W, n, m)
+    assert np.array_equal(host(mask_d), mask)
+    _check_quant(W, mask, flags, packed, scale, sb)
+
+
+def test_quant_edge_rows(sbl):
+    W = synth.latent_weight("gpu/quant/edge", 6, 256)
+    W[0] = 0.0                       # all-zero row: gamma clamps to 1e-5
+    W[1] = 1e-9                      # mean below the clamp
+    W[2, :] = 0.02                   # all equal: every |w| > gamma/2
+    W[3] = tie_heavy("gpu/quant/edge3", 1, 256)
+    W[4, ::2] = 0.0
+    mask_d, packed, scale, sb = sbl.nm_mask_quant_pack(dev(W), 3, 4)
+    mask = oracle.nm_mask(W, 3, 4)
+    assert np.array_equal(host(mask_d), mask)
+    _check_quant(W, mask, 0, packed, scale, sb)
+    assert host(scale)[0] == np.float32(1e-5) and host(scale)[1] == np.float32(1e-5)
+
+
+def test_quant_exact_half_boundaries(sbl):
+    """Weights placed exactly at and one ulp around gamma/2 of their row."""
+    rows, cols = 8, 256
+    W = synth.latent_weight("gpu/quant/half", rows, cols)
+    g, _ = oracle.row_scale(W)
+    rng = synth.rng("gpu/quant/half/pos")
+    for r in range(rows):
+        h = np.float32(g[r] / np.float32(2))
+        for j in rng.choice(cols, 24, replace=False):
+            W[r, j] = rng.choice([h, np.nextafter(h, np.float32(0)), np.nextafter(h, np.float32(1)), -h])
+    # placing values moved the mean; iterate once more so some stay on the boundary
+    g2, _ = oracle.row_scale(W)
+    packed, scale, sb = sbl.ternary_quant_pack(dev(W))
+    _check_quant(W, None, 0, packed, scale, sb)
+
+
+def test_grouped_refresh(sbl):
+    shapes = [(896, 896), (128, 896), (4864, 896), (896, 4864), (64, 256)]
+    jobs, refs = [], []
+    for i, (r, c) in enumerate(shapes):
+        W = synth.latent_weight(f"gpu/grouped/{i}", r, c)
+        Wd = dev(W)
+        jobs.append(dict(W=Wd, mask=torch.empty(r * c // 8, dtype=torch.uint8, device=DEV),
+                         packed=torch.empty((r, c // 4), dtype=torch.uint8, device=DEV),
+                         scale=torch.empty(r, dtype=torch.float32, device=DEV),
+                         scale_bf16=torch.empty(r, dtype=torch.int16, device=DEV)))
+        refs.append(W)
+    keep = sbl.nm_mask_quant_pack_grouped(jobs, 3, 4)
+    torch.cuda.synchronize()
+    del keep
+    for W, j in zip(refs, jobs):
+        mask = oracle.nm_mask(W, 3, 4)
+        assert np.array_equal(host(j["mask"]), mask)
+        _check_quant(W, mask, 0, j["packed"], j["scale"], j["scale_bf16"])
+
+
+# -------------------------------------------------------------- act quant
+@pytest.mark.parametrize("T,K", [(1, 64), (3, 256), (128, 896), (77, 4864), (5, 8192), (4, 9216)])
+def test_act_quant(sbl, T, K):
+    x = synth.activations_bf16(f"gpu/act/{T}x{K}", T, K)
+    x[0, : min(K, 8)] = 0  # a few exact zeros
+    xq, beta = sbl.act_quant_i8(dev(x))
+    xq_ref, b_ref = oracle.act_quant(x)
+    assert np.array_equal(host(xq), xq_ref)
+    assert np.array_equal(host(beta), b_ref)
+
+
+def test_act_quant_edge_tokens(sbl):
+    x = synth.activations_bf16("gpu/act/edge", 4, 256)
+    x[0] = 0                            # zero token: beta = 1e-5
+    x[1] = 0x8000                       # all -0.0
+    vals = np.array([127, 0.5, 1.5, 2.5, -0.5, -2.5, 3.5, -126.5], dtype=np.float32)
+    x[2, :8] = synth.float_to_bf16_bits(vals)  # beta = 127: exact .5 ties
+    x[2, 8:] = 0
+    x[3] = synth.float_to_bf16_bits(np.full(256, -3.0, np.float32))
+    xq, beta = sbl.act_quant_i8(dev(x))
+    xq_ref, b_ref = oracle.act_quant(x)
+    assert np.array_equal(host(xq), xq_ref)
+    assert np.array_equal(host(beta), b_ref)
+    assert host(xq)[2, :8].tolist() == [127, 0, 2, 2, 0, -2, 4, -126]
+
+
+# -------------------------------------------------------------- products
+def _operands(tag, T, K, N, n=3, m=4):
+    W = synth.latent_weight(f"{tag}/W", N, K)
+    x = synth.activations_bf16(f"{tag}/x", T, K)
+    mask = oracle.nm_mask(W, n, m)
+    g, gb = oracle.row_scale(W)
+    codes = oracle.ternary_codes(W, mask, g)
+    packed = oracle.pack_codes(codes)
+    xq, beta = oracle.act_quant(x)
+    return dict(codes=codes, packed=packed, g=g, gb=gb, xq=xq, beta=beta)
+
+
+GEMM_SHAPES = [(128, 256, 512), (300, 896, 200), (257, 448, 1152), (33, 64, 4), (1, 64, 1),
+               (5, 128, 7), (130, 896, 128), (129, 4864, 260), (64, 2048, 2048)]
+
+
+@pytest.mark.parametrize("T,K,N", GEMM_SHAPES)
+@pytest.mark.parametrize("bf16_scale", [False, True])
+def test_gemm(sbl, T, K, N, bf16_scale):
+    o = _operands(f"gpu/gemm/{T}x{K}x{N}", T, K, N)
+    scale = dev(o["gb"]) if bf16_scale else dev(o["g"])
+    y, acc = sbl.sparse_bitlinear_gemm(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), scale,
+                                       want_acc=True)
+    acc_ref = oracle.gemm_acc(o["xq"], o["codes"])
+    assert np.array_equal(host(acc), acc_ref)
+    g_used = oracle.bf16_bits_to_float(o["gb"]) if bf16_scale else o["g"]
+    assert_y_close(host(y), oracle.dequant(acc_ref, o["beta"], g_used))
+
+
+def test_gemm_extreme_operands(sbl):
+    """All-127 / all -128 activations against all +-1 codes: the largest
+    accumulators the contract allows at this K."""
+    T, K, N = 64, 4864, 64
+    xq = np.full((T, K), 127, np.int8)
+    xq[1::2] = -128
+    codes = np.ones((N, K), np.int8)
+    codes[1::2] = -1
+    codes[2::4, ::3] = 0
+    packed = oracle.pack_codes(codes)
+    beta = np.ones(T, np.float32)
+    g = np.full(N, 0.02, np.float32)
+    y, acc = sbl.sparse_bitlinear_gemm(dev(xq), dev(beta), dev(packed), dev(g), want_acc=True)
+    acc_ref = oracle.gemm_acc(xq, codes)
+    assert np.array_equal(host(acc), acc_ref)
+    assert_y_close(host(y), oracle.dequant(acc_ref, beta, g))
+
+
+@pytest.mark.parametrize("name,N,K", [("q", 896, 896), ("k", 128, 896), ("gate", 4864, 896),
+                                      ("down", 896, 4864), ("wide_up", 7168, 2048),
+                                      ("wide_down", 2048, 7168)])
+def test_full_size_layer_sampled(sbl, name, N, K):
+    """Full-size prefill shapes (32768 tokens for the 0.5B skeleton, 8192 for
+    the 2048/7168 stack), run end to end on the GPU; weights, codes and
+    scales compared in full, x~ in full, acc and y on 96 sampled tokens."""
+    T = 8192 if name.startswith("wide") else 32768
+    W = synth.latent_weight(f"cfg/full/{name}/W", N, K)
+    x = synth.activations_bf16(f"cfg/full/{name}/x", T, K)
+    mask_d, packed_d, scale_d, sb_d = sbl.nm_mask_quant_pack(dev(W), 3, 4)
+    xq_d, beta_d = sbl.act_quant_i8(dev(x))
+    y_d, acc_d = sbl.sparse_bitlinear_gemm(xq_d, beta_d, packed_d, scale_d, want_acc=True)
+    mask = oracle.nm_mask(W, 3, 4)
+    g, gb = oracle.row_scale(W)
+    codes = oracle.ternary_codes(W, mask, g)
+    assert np.array_equal(host(mask_d), mask)
+    assert np.array_equal(host(packed_d), oracle.pack_codes(codes))
+    assert np.array_equal(host(scale_d), g)
+    xq, beta = oracle.act_quant(x)
+    assert np.array_equal(host(xq_d), xq)
+    assert np.array_equal(host(beta_d), beta)
+    rows = np.sort(synth.rng(f"cfg/full/{name}/sample").choice(T, 96, replace=False))
+    rows[-1] = T - 1
+    acc_ref = oracle.gemm_acc(xq[rows], codes)
+    assert np.array_equal(host(acc_d)[rows], acc_ref)
+    assert_y_close(host(y_d)[rows], oracle.dequant(acc_ref, beta[rows], g))
+
+
+# ------------------------------------------------------------------ 2:4
+@pytest.mark.parametrize("T,K,N", [(128, 256, 512), (300, 896, 200), (65, 4864, 896), (7, 64, 36)])
+def test_sparse24_matches_dense(sbl, T, K, N):
+    o = _operands(f"gpu/sp24/{T}x{K}x{N}", T, K, N, n=2, m=4)
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sp = sbl.sparse24_compress(dev(o["packed"]), bad)
+    y, acc = sbl.sparse_bitlinear_gemm_sparse24(dev(o["xq"]), dev(o["beta"]), sp, N, dev(o["g"]),
+                                                want_acc=True)
+    yd, accd = sbl.sparse_bitlinear_gemm(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]),
+                                         dev(o["g"]), want_acc=True)
+    assert int(bad.item()) == 0
+    acc_ref = oracle.gemm_acc(o["xq"], o["codes"])
+    assert np.array_equal(host(acc), acc_ref)
+    assert np.array_equal(host(accd), acc_ref)
+    assert np.array_equal(host(y), host(yd))
+    assert_y_close(host(y), oracle.dequant(acc_ref, o["beta"], o["g"]))
+
+
+def test_sparse24_counts_groups_that_are_not_2of4(sbl):
+    o = _operands("gpu/sp24/bad", 16, 256, 64, n=3, m=4)
+    nz = (o["codes"].reshape(64, -1, 4) != 0).sum(-1)
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sbl.sparse24_compress(dev(o["packed"]), bad)
+    assert int(bad.item()) == int((nz > 2).sum())
+
+
+# ---------------------------------------------------------------- decode
+@pytest.mark.parametrize("T", [1, 4, 16, 3])
+@pytest.mark.parametrize("N,K", [(512, 256), (896, 896), (128, 896), (4864, 896), (896, 4864),
+                                 (100, 192), (2048, 7168)])
+def test_gemv(sbl, T, N, K):
+    o = _operands(f"gpu/gemv/{N}x{K}", T, K, N)
+    y = sbl.sparse_bitlinear_gemv(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), dev(o["gb"]))
+    acc_ref = oracle.gemm_acc(o["xq"], o["codes"])
+    assert_y_close(host(y), oracle.dequant(acc_ref, o["beta"], oracle.bf16_bits_to_float(o["gb"])))
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_gemv_grouped(sbl, T):
+    shapes = [("q", 896, 896), ("k", 128, 896), ("v", 128, 896), ("o", 896, 896),
+              ("gate", 4864, 896), ("up", 4864, 896), ("down", 896, 4864), ("tiny", 36, 64)]
+    jobs, refs = [], []
+    for name, N, K in shapes:
+        o = _operands(f"gpu/gemvg/{name}", T, K, N, n=2 if name == "o" else 3)
+        jobs.append(dict(xq=dev(o["xq"]), beta=dev(o["beta"]), packed=dev(o["packed"]),
+                         scale=dev(o["gb"]) if name != "v" else dev(o["g"]),
+                         y=torch.full((T, N), float("nan"), device=DEV)))
+        refs.append(o)
+    hostd, devd = sbl.gemv_descs(jobs)
+    sbl.sparse_bitlinear_gemv_grouped(hostd, devd, len(jobs), T, DEV)
+    torch.cuda.synchronize()
+    for (name, N, K), j, o in zip(shapes, jobs, refs):
+        g = o["g"] if name == "v" else oracle.bf16_bits_to_float(o["gb"])
+        acc_ref = oracle.gemm_acc(o["xq"], o["codes"])
+        assert_y_close(host(j["y"]), oracle.dequant(acc_ref, o["beta"], g))
+
+
+# ------------------------------------------------------------- plumbing
+def test_empty_inputs_are_noops(sbl):
+    x = torch.empty((0, 64), dtype=torch.int16, device=DEV)
+    xq, beta = sbl.act_quant_i8(x)
+    assert xq.shape == (0, 64)
+    W = torch.empty((0, 64), dtype=torch.float32, device=DEV)
+    _, packed, scale, _ = sbl.nm_mask_quant_pack(W, 3, 4)
+    assert packed.shape == (0, 16)
+    y, _ = sbl.sparse_bitlinear_gemm(torch.empty((0, 64), dtype=torch.int8, device=DEV),
+                                     torch.empty(0, device=DEV),
+                                     torch.zeros((8, 16), dtype=torch.uint8, device=DEV),
+                                     torch.ones(8, device=DEV))
+    assert y.shape == (0, 8)
+
+
+def test_errors_raise(sbl):
+    W = torch.zeros((4, 96), dtype=torch.float32, device=DEV)
+    with pytest.raises(sbl.SblError):
+        sbl.nm_mask_create(W, 2, 4)
+    x = torch.zeros((20, 64), dtype=torch.int8, device=DEV)
+    with pytest.raises(sbl.SblError):
+        sbl.sparse_bitlinear_gemv(x, torch.ones(20, device=DEV),
+                                  torch.zeros((8, 16), dtype=torch.uint8, device=DEV),
+                                  torch.ones(8, device=DEV))
+
+
+def test_repeat_runs_are_bitwise_identical(sbl):
+    o = _operands("gpu/repeat", 1000, 896, 896)
+    args = (dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), dev(o["g"]))
+    y1, a1 = sbl.sparse_bitlinear_gemm(*args, want_acc=True)
+    y2, a2 = sbl.sparse_bitlinear_gemm(*args, want_acc=True)
+    assert torch.equal(y1, y2) and torch.equal(a1, a2)
