@@ -1,0 +1,443 @@
+"""Benchmark of the Sparse-BitLinear forward path on one MI355X.
+
+A step is one forward pass of the whole hot path over one layer of the
+Qwen2.5-0.5B skeleton (3:4, 32768 prefill tokens = 16 x 2048), with every
+input already resident in HBM:
+  * mask + absmean quantise + pack of the 7 latent fp32 weight matrices
+    (q, k, v, o, gate, up, down) in one grouped launch,
+  * int8 quantisation of the 4 activation inputs of the layer (attention
+    input for q/k/v, attention output for o, MLP input for gate/up, MLP
+    hidden state for down),
+  * the 7 packed-ternary x int8 prefill products (fp32 outputs).
+`value` is the int8 TOPS of the step: dense-equivalent ops 2*T*N*K of the 7
+products divided by the step time (mask, quantisation and activation
+passes included in the time).
+
+The same run also measures, outside the timed step and reported under
+"extra": each kernel's own rate against its roofline, the decode sweep
+(168 grouped GEMVs, batch 1/4/16, cold across rotated weight copies), the
+2:4 smfmac product against the dense-expanded one, the 2048/7168 stack
+(full-model refresh and 8192-token products) and the tiny 256->512 layer.
+The CPU oracle is timed on a bounded sample of the step on the host cores.
+
+Inputs are synthetic (seeded N(0, 0.02) fp32 weights, N(0, 1) bf16
+activations); no dataset or checkpoint is involved.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_I8_TOPS = 5000.0      # MI355X dense int8 matrix peak (5.0 POP/s)
+METRIC = "Sparse-BitLinear int8 TOPS (prefill) + HBM GB/s (decode), 3:4 @ d896/ffn4864"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target host time of the oracle sample")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on torch's current stream, which is the stream every libsbl
+    call of this benchmark is launched on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time(self, fn, iters, warmup=2, flush=None):
+        torch = self.torch
+        for _ in range(warmup):
+            if flush:
+                flush()
+            fn()
+        evs = []
+        for i in range(iters):
+            if flush:
+                flush()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(i)
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in evs])
+        return float(np.median(ms)), float(np.mean(ms))
+
+
+def kernel_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_linear_layers_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, sha):
+    """HBM bytes per launch measured with rocprofv3 counters, if the
+    recorded kernel source still matches."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        e = t.get(kernel)
+        if e and e.get("sha") == sha:
+            return e
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+# --------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_linear_layers_amd as sbl
+    from sparse_linear_layers_amd import synth
+
+    sbl.load()
+    dev = torch.device("cuda:0")
+    timer = Timer(torch)
+    T = synth.QWEN05B_PREFILL_TOKENS
+    linears = synth.QWEN05B_LINEARS
+    n, m = 3, 4
+
+    # ---------------- inputs for one layer (resident in HBM) ----------------
+    log("[bench] generating inputs")
+    t0 = time.time()
+    W = {name: torch.from_numpy(synth.latent_weight(f"cfg2/L0/{name}/W", N, K)).to(dev)
+         for name, N, K in linears}
+    xin_names = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "attn_out",
+                 "gate": "mlp_in", "up": "mlp_in", "down": "mlp_hidden"}
+    xin_K = {"attn_in": 896, "attn_out": 896, "mlp_in": 896, "mlp_hidden": 4864}
+    xs = {}
+    for xn, K in xin_K.items():
+        xs[xn] = torch.from_numpy(synth.activations_bf16(f"cfg2/L0/{xn}/x", T, K).view(np.int16)).to(dev)
+    packed = {name: torch.empty((N, K // 4), dtype=torch.uint8, device=dev) for name, N, K in linears}
+    scale = {name: torch.empty(N, dtype=torch.float32, device=dev) for name, N, K in linears}
+    xq = {xn: torch.empty((T, K), dtype=torch.int8, device=dev) for xn, K in xin_K.items()}
+    beta = {xn: torch.empty(T, dtype=torch.float32, device=dev) for xn in xin_K}
+    y = {name: torch.empty((T, N), dtype=torch.float32, device=dev) for name, N, K in linears}
+    rjobs = [dict(W=W[name], packed=packed[name], scale=scale[name]) for name, _, _ in linears]
+    rhost, rdev = sbl.refresh_descs(rjobs)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
+
+    def refresh():
+        sbl.nm_mask_quant_pack_grouped(rhost, rdev, len(rjobs), n, m, 0, dev)
+
+    def quant_acts():
+        for xn in xin_K:
+            sbl.act_quant_i8(xs[xn], xq[xn], beta[xn])
+
+    def gemm(name):
+        sbl.sparse_bitlinear_gemm(xq[xin_names[name]], beta[xin_names[name]], packed[name],
+                                  scale[name], y=y[name])
+
+    def step(_=None):
+        refresh()
+        quant_acts()
+        for name, _, _ in linears:
+            gemm(name)
+
+    gemm_ops = sum(2.0 * T * N * K for _, N, K in linears)
+
+    # ---------------- timed region ----------------
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t_start = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    tops = gemm_ops / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] {ms_per_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f}), {tops:.1f} TOPS")
+
+    # ---------------- per-kernel rates (dominant kernel: the product) -------
+    per_shape = {}
+    tot_ms, tot_ops = 0.0, 0.0
+    for name, N, K in linears:
+        med, mean = timer.time(lambda i=0, nm=name: gemm(nm), 20)
+        ops = 2.0 * T * N * K
+        byts = T * K + N * K / 4 + 4 * N + 4 * T + 4.0 * T * N
+        attain = min(PEAK_I8_TOPS, PEAK_HBM_GBS * 1e9 * ops / byts / 1e12)
+        per_shape[name] = dict(N=N, K=K, T=T, us=mean * 1e3, tops=ops / (mean * 1e-3) / 1e12,
+                               gbs=byts / (mean * 1e-3) / 1e9,
+                               frac_mfma_peak=ops / (mean * 1e-3) / 1e12 / PEAK_I8_TOPS,
+                               frac_attainable=ops / (mean * 1e-3) / 1e12 / attain)
+        tot_ms += mean
+        tot_ops += ops
+    gemm_tops = tot_ops / (tot_ms * 1e-3) / 1e12
+    sha = kernel_sha("gemm.hip", "sbl_device.h")
+    tr = load_traffic("gemm_i8_kernel", sha)
+    roofline = {"kernel": "gemm_i8_kernel (7 prefill products of the layer, mean per launch)",
+                "bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_I8_TOPS,
+                "unit": "TFLOP/s", "op": "int8 ops (2*T*N*K, dense-equivalent)",
+                "frac": round(gemm_tops / PEAK_I8_TOPS, 4),
+                "traffic": tr["bytes_per_launch"] if tr else None,
+                "avg_launch_us": round(tot_ms * 1e3 / len(linears), 2)}
+
+    med_r, mean_r = timer.time(lambda i=0: refresh(), 20)
+    nw = sum(N * K for _, N, K in linears)
+    nrows = sum(N for _, N, _ in linears)
+    refresh_bytes = 4.25 * nw + 4 * nrows
+    med_a, mean_a = timer.time(lambda i=0: quant_acts(), 20)
+    act_bytes = sum(3.0 * T * K + 4 * T for K in xin_K.values())
+    extra = {
+        "step_breakdown_us": {"refresh": round(mean_r * 1e3, 2), "act_quant": round(mean_a * 1e3, 2),
+                              "gemm_total": round(tot_ms * 1e3, 2)},
+        "gemm_per_shape": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                               for kk, vv in v.items()} for k, v in per_shape.items()},
+        "refresh_grouped": {"weights": nw, "us": round(mean_r * 1e3, 2),
+                            "gbs": round(refresh_bytes / (mean_r * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(refresh_bytes / (mean_r * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "act_quant": {"us": round(mean_a * 1e3, 2),
+                      "gbs": round(act_bytes / (mean_a * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(act_bytes / (mean_a * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+
+    if not args.no_extra:
+        extra.update(secondary(torch, sbl, synth, dev, timer))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(synth, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "Qwen2.5-0.5B-skeleton layer set, 3:4, 32768-token prefill "
+                               "(q/k/v/o/gate/up/down; mask+quant+pack, act quant, 7 products)",
+                   "tokens": T, "d_model": 896, "d_ffn": 4864, "kv_width": 128, "n": n, "m": m},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+# --------------------------------------------------------------------------
+def secondary(torch, sbl, synth, dev, timer):
+    res = {}
+    # ---- decode sweep: 24 layers x 7 linears, bf16 row scales ----
+    log("[bench] decode sweep setup")
+    L = synth.QWEN05B_LAYERS
+    mats = []
+    for layer in range(L):
+        for name, N, K in synth.QWEN05B_LINEARS:
+            mats.append((layer, name, N, K))
+    # latent weights -> packed codes on the GPU (one layer's worth at a time)
+    packed0, scales0 = [], []
+    for (layer, name, N, K) in mats:
+        Wl = torch.from_numpy(synth.latent_weight(f"cfg4/L{layer}/{name}/W", N, K)).to(dev)
+        _, p, s, sb = sbl.nm_mask_quant_pack(Wl, 3, 4, want_mask=False)
+        packed0.append(p)
+        scales0.append(sb)
+        del Wl
+    torch.cuda.synchronize()
+    # six copies of the whole packed set (6 x 90 MB > 2 x the 256 MB Infinity
+    # Cache) so that consecutive sweeps read weights from HBM
+    ROT = 6
+    sets = [[p.clone() for p in packed0] for _ in range(ROT)]
+    code_bytes = sum(p.numel() for p in packed0)
+    dec = {}
+    for B in synth.DECODE_BATCHES:
+        x_by_K = {}
+        for K in (896, 4864):
+            xb = torch.from_numpy(synth.activations_bf16(f"cfg4/x/{K}/B{B}", B, K).view(np.int16)).to(dev)
+            x_by_K[K] = sbl.act_quant_i8(xb)
+        ys = [torch.empty((B, N), dtype=torch.float32, device=dev) for (_, _, N, _) in mats]
+        descs = []
+        for r in range(ROT):
+            jobs = [dict(xq=x_by_K[K][0], beta=x_by_K[K][1], packed=sets[r][i], scale=scales0[i],
+                         y=ys[i]) for i, (_, _, N, K) in enumerate(mats)]
+            descs.append(sbl.gemv_descs(jobs))
+
+        def sweep(i=0, B=B, descs=descs):
+            h, d = descs[i % ROT]
+            sbl.sparse_bitlinear_gemv_grouped(h, d, len(mats), B, dev)
+
+        med, mean = timer.time(sweep, 60, warmup=ROT)
+        byts = code_bytes + sum(2 * N + B * K + 4 * B + 4 * B * N for (_, _, N, K) in mats)
+        # warm: the same copy every time
+        medw, meanw = timer.time(lambda i=0: sweep(0), 30)
+        dec[f"B{B}"] = {"us": round(mean * 1e3, 2), "gbs": round(byts / (mean * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(byts / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "bytes": int(byts), "warm_us": round(meanw * 1e3, 2),
+                        "warm_gbs": round(byts / (meanw * 1e-3) / 1e9, 1)}
+        log(f"[bench] decode B={B}: {dec[f'B{B}']}")
+    res["decode_sweep_3of4"] = dec
+    del sets, packed0
+    torch.cuda.empty_cache()
+
+    # ---- 2:4: smfmac vs dense-expanded, identical seeded inputs ----
+    log("[bench] 2:4 products")
+    T = synth.QWEN05B_PREFILL_TOKENS
+    sp = {}
+    xcache = {}
+    for name, N, K in synth.QWEN05B_LINEARS:
+        Wl = torch.from_numpy(synth.latent_weight(f"cfg2/L0/{name}/W", N, K)).to(dev)
+        _, p, s, _ = sbl.nm_mask_quant_pack(Wl, 2, 4, want_mask=False, want_bf16=False)
+        if K not in xcache:
+            xb = torch.from_numpy(synth.activations_bf16(f"cfg3/x/{K}", T, K).view(np.int16)).to(dev)
+            xcache[K] = sbl.act_quant_i8(xb)
+        xqK, bK = xcache[K]
+        img = sbl.sparse24_compress(p)
+        yv = torch.empty((T, N), dtype=torch.float32, device=dev)
+        _, md = timer.time(lambda i=0: sbl.sparse_bitlinear_gemm(xqK, bK, p, s, y=yv), 10)
+        _, ms = timer.time(lambda i=0: sbl.sparse_bitlinear_gemm_sparse24(xqK, bK, img, N, s, y=yv), 10)
+        ops = 2.0 * T * N * K
+        sp[name] = {"dense_us": round(md * 1e3, 2), "smfmac_us": round(ms * 1e3, 2),
+                    "dense_tops": round(ops / (md * 1e-3) / 1e12, 1),
+                    "smfmac_tops": round(ops / (ms * 1e-3) / 1e12, 1)}
+        del Wl
+    res["prefill_2of4_smfmac_vs_dense"] = sp
+    log(f"[bench] 2:4: {sp}")
+    del xcache
+    torch.cuda.empty_cache()
+
+    # ---- 2048/7168 stack: full-model refresh + 8192-token products ----
+    log("[bench] wide stack setup")
+    Tw = synth.WIDE_PREFILL_TOKENS
+    jobs = []
+    for layer in range(synth.WIDE_LAYERS):
+        for name, N, K in synth.WIDE_LINEARS:
+            Wl = torch.from_numpy(synth.latent_weight(f"cfg5/L{layer}/{name}/W", N, K)).to(dev)
+            jobs.append(dict(W=Wl, packed=torch.empty((N, K // 4), dtype=torch.uint8, device=dev),
+                             scale=torch.empty(N, dtype=torch.float32, device=dev)))
+    h, d = sbl.refresh_descs(jobs)
+    torch.cuda.synchronize()
+    _, mr = timer.time(lambda i=0: sbl.nm_mask_quant_pack_grouped(h, d, len(jobs), 3, 4, 0, dev), 5)
+    nw = sum(j["W"].numel() for j in jobs)
+    nr = sum(j["W"].shape[0] for j in jobs)
+    rb = 4.25 * nw + 4 * nr
+    wide = {"refresh": {"weights": nw, "us": round(mr * 1e3, 1), "gbs": round(rb / (mr * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(rb / (mr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+    g = {}
+    for name, N, K in synth.WIDE_LINEARS[3:]:  # o (2048x2048), gate, up, down
+        j = jobs[[nm for nm, _, _ in synth.WIDE_LINEARS].index(name)]
+        xb = torch.from_numpy(synth.activations_bf16(f"cfg5/x/{K}", Tw, K).view(np.int16)).to(dev)
+        xqK, bK = sbl.act_quant_i8(xb)
+        yv = torch.empty((Tw, N), dtype=torch.float32, device=dev)
+        _, mg = timer.time(lambda i=0: sbl.sparse_bitlinear_gemm(xqK, bK, j["packed"], j["scale"], y=yv), 10)
+        ops = 2.0 * Tw * N * K
+        g[f"{name}_{N}x{K}"] = {"us": round(mg * 1e3, 2), "tops": round(ops / (mg * 1e-3) / 1e12, 1),
+                                "frac_mfma_peak": round(ops / (mg * 1e-3) / 1e12 / PEAK_I8_TOPS, 4)}
+    wide["gemm"] = g
+    res["wide_2048_7168"] = wide
+    log(f"[bench] wide: {wide}")
+    del jobs
+    torch.cuda.empty_cache()
+
+    # ---- tiny 256 -> 512 layer: the whole pipeline ----
+    Wt = torch.from_numpy(synth.latent_weight("cfg1/W", 512, 256)).to(dev)
+    xt = torch.from_numpy(synth.activations_bf16("cfg1/x", 128, 256).view(np.int16)).to(dev)
+    outs = sbl.nm_mask_quant_pack(Wt, 3, 4, want_mask=False, want_bf16=False)
+    xqt, bt = sbl.act_quant_i8(xt)
+    yt = torch.empty((128, 512), dtype=torch.float32, device=dev)
+
+    def tiny(i=0):
+        sbl.nm_mask_quant_pack(Wt, 3, 4, out=outs)
+        sbl.act_quant_i8(xt, xqt, bt)
+        sbl.sparse_bitlinear_gemm(xqt, bt, outs[1], outs[2], y=yt)
+
+    _, mt = timer.time(tiny, 50)
+    res["tiny_256x512_T128"] = {"pipeline_us": round(mt * 1e3, 2)}
+    return res
+
+
+# --------------------------------------------------------------------------
+def cpu_baseline(synth, seconds):
+    """The oracle, as it stands, on the host cores: one layer's mask +
+    quantise + pack in full, then activation quantisation and the integer
+    products with rescale on a token sample sized to about `seconds`."""
+    import oracle
+
+    log("[bench] cpu baseline (oracle)")
+    linears = synth.QWEN05B_LINEARS
+    Ws = {name: synth.latent_weight(f"cfg2/L0/{name}/W", N, K) for name, N, K in linears}
+    t0 = time.perf_counter()
+    codes, gam = {}, {}
+    for name, N, K in linears:
+        mk = oracle.nm_mask(Ws[name], 3, 4)
+        g, _ = oracle.row_scale(Ws[name])
+        codes[name] = oracle.ternary_codes(Ws[name], mk, g)
+        oracle.pack_codes(codes[name])
+        gam[name] = g
+    t_refresh = time.perf_counter() - t0
+    xin = {"q": 896, "k": 896, "v": 896, "o": 896, "gate": 896, "up": 896, "down": 4864}
+
+    def run(tok):
+        xb = {K: synth.activations_bf16(f"cfg2/cpu/x/{K}", tok, K) for K in (896, 4864)}
+        t = time.perf_counter()
+        xq = {K: oracle.act_quant(v) for K, v in xb.items()}
+        for name, N, K in linears:
+            acc = oracle.gemm_acc(xq[xin[name]][0], codes[name])
+            oracle.dequant(acc, xq[xin[name]][1], gam[name])
+        return time.perf_counter() - t
+
+    tok = 64
+    dt = run(tok)
+    while dt < seconds / 4 and tok < 32768:
+        tok = min(32768, tok * 4 if dt < seconds / 16 else tok * 2)
+        dt = run(tok)
+    ops = sum(2.0 * tok * N * K for _, N, K in linears)
+    T = synth.QWEN05B_PREFILL_TOKENS
+    # scale the refresh (done once per step, full size) into the step time
+    step_s = dt * (T / tok) + t_refresh
+    full_ops = sum(2.0 * T * N * K for _, N, K in linears)
+    return {"value": round(full_ops / step_s / 1e12, 5), "unit": "TOPS",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"one 0.5B-skeleton layer, 3:4: mask+quant+pack of all 7 matrices in full "
+                      f"({t_refresh:.2f} s), act quant + 7 products + rescale on {tok} of {T} "
+                      f"tokens ({dt:.2f} s), scaled to the full step",
+            "sample_ops_per_s": round(ops / dt / 1e12, 5)}
+
+
+if __name__ == "__main__":
+    main()

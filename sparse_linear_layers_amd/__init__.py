@@ -26,7 +26,7 @@ __all__ = [
     "nm_mask_quant_pack", "nm_mask_quant_pack_grouped", "act_quant_i8",
     "sparse_bitlinear_gemm", "sparse24_bytes", "sparse24_compress",
     "sparse_bitlinear_gemm_sparse24", "sparse_bitlinear_gemv",
-    "sparse_bitlinear_gemv_grouped", "GemvDesc", "RefreshDesc",
+    "sparse_bitlinear_gemv_grouped", "GemvDesc", "RefreshDesc", "refresh_descs", "gemv_descs",
     "SCALE_FROM_MASKED", "SCALE_F32", "SCALE_BF16", "GEMV_MAX_TOKENS",
 ]
 
@@ -158,15 +158,19 @@ def ternary_quant_pack(W: torch.Tensor, mask_bits: torch.Tensor | None = None,
 
 
 def nm_mask_quant_pack(W: torch.Tensor, n: int, m: int, flags: int = 0,
-                       want_mask: bool = True, want_bf16: bool = True):
-    """-> (mask bits or None, packed, scale, scale_bf16 or None)."""
+                       want_mask: bool = True, want_bf16: bool = True, out=None):
+    """-> (mask bits or None, packed, scale, scale_bf16 or None); `out` may
+    pass that tuple preallocated."""
     _need(W, torch.float32, "W", 2)
     rows, cols = W.shape
     dev = W.device
-    mask = torch.empty(rows * cols // 8, dtype=torch.uint8, device=dev) if want_mask else None
-    packed = torch.empty((rows, cols // 4), dtype=torch.uint8, device=dev)
-    scale = torch.empty(rows, dtype=torch.float32, device=dev)
-    sb = torch.empty(rows, dtype=torch.int16, device=dev) if want_bf16 else None
+    if out is not None:
+        mask, packed, scale, sb = out
+    else:
+        mask = torch.empty(rows * cols // 8, dtype=torch.uint8, device=dev) if want_mask else None
+        packed = torch.empty((rows, cols // 4), dtype=torch.uint8, device=dev)
+        scale = torch.empty(rows, dtype=torch.float32, device=dev)
+        sb = torch.empty(rows, dtype=torch.int16, device=dev) if want_bf16 else None
     _check("nm_mask_quant_pack", load().nm_mask_quant_pack(
         _ptr(W), rows, cols, n, m, flags, _ptr(mask), _ptr(packed), _ptr(scale), _ptr(sb),
         _stream(dev)))
@@ -181,12 +185,10 @@ def _desc_array(descs, cls, device):
     return host, dev
 
 
-def nm_mask_quant_pack_grouped(jobs, n: int, m: int, flags: int = 0):
-    """jobs: list of dicts with W, packed, scale and optional mask, scale_bf16
-    tensors (all preallocated).  One launch over all of them."""
-    if not jobs:
-        return
-    dev = jobs[0]["W"].device
+def refresh_descs(jobs):
+    """(host array, device tensor) descriptors for nm_mask_quant_pack_grouped
+    from dicts with preallocated W, packed, scale and optional mask and
+    scale_bf16 tensors."""
     ds = []
     for j in jobs:
         W = _need(j["W"], torch.float32, "W", 2)
@@ -195,18 +197,27 @@ def nm_mask_quant_pack_grouped(jobs, n: int, m: int, flags: int = 0):
                               j["packed"].data_ptr(), j["scale"].data_ptr(),
                               sb.data_ptr() if sb is not None else None,
                               W.shape[0], W.shape[1]))
-    host, devbuf = _desc_array(ds, RefreshDesc, dev)
+    return _desc_array(ds, RefreshDesc, jobs[0]["W"].device)
+
+
+def nm_mask_quant_pack_grouped(host, devbuf, count: int, n: int, m: int, flags: int,
+                               device) -> None:
+    """One launch of mask + quantise + pack over every descriptor (see
+    refresh_descs).  The device descriptors must stay alive until the stream
+    passes the launch."""
     _check("nm_mask_quant_pack_grouped", load().nm_mask_quant_pack_grouped(
-        ctypes.cast(host, ctypes.c_void_p), _ptr(devbuf), len(ds), n, m, flags, _stream(dev)))
-    return devbuf  # keep alive until the stream passes the launch
+        ctypes.cast(host, ctypes.c_void_p), _ptr(devbuf), count, n, m, flags, _stream(device)))
 
 
-def act_quant_i8(x: torch.Tensor):
+def act_quant_i8(x: torch.Tensor, xq: torch.Tensor | None = None,
+                 beta: torch.Tensor | None = None):
     """x bfloat16 [tokens, cols] -> (xq int8 [tokens, cols], beta float32 [tokens])."""
     _need(x, _BF16_BITS, "x", 2)
     T, K = x.shape
-    xq = torch.empty((T, K), dtype=torch.int8, device=x.device)
-    beta = torch.empty(T, dtype=torch.float32, device=x.device)
+    if xq is None:
+        xq = torch.empty((T, K), dtype=torch.int8, device=x.device)
+    if beta is None:
+        beta = torch.empty(T, dtype=torch.float32, device=x.device)
     _check("act_quant_i8", load().act_quant_i8(_ptr(x), T, K, _ptr(xq), _ptr(beta),
                                                _stream(x.device)))
     return xq, beta
@@ -222,6 +233,7 @@ def _scale_dtype(scale):
 
 def sparse_bitlinear_gemm(xq, beta, packed, scale, want_acc: bool = False,
                           y: torch.Tensor | None = None):
+    # (y may be preallocated [T, N] float32)
     """-> (y float32 [T, N], acc int32 [T, N] or None)."""
     _need(xq, torch.int8, "xq", 2)
     _need(beta, torch.float32, "beta", 1)
@@ -245,11 +257,13 @@ def sparse24_bytes(N: int, K: int) -> int:
     return int(load().sparse24_bytes(N, K))
 
 
-def sparse24_compress(packed: torch.Tensor, bad_groups: torch.Tensor | None = None):
+def sparse24_compress(packed: torch.Tensor, bad_groups: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None):
     """packed uint8 [N, K/4] (2:4 codes) -> private smfmac operand image."""
     _need(packed, torch.uint8, "packed", 2)
     N, K = packed.shape[0], packed.shape[1] * 4
-    out = torch.empty(max(sparse24_bytes(N, K), 16), dtype=torch.uint8, device=packed.device)
+    if out is None:
+        out = torch.empty(max(sparse24_bytes(N, K), 16), dtype=torch.uint8, device=packed.device)
     _check("sparse24_compress", load().sparse24_compress(
         _ptr(packed), N, K, _ptr(out), _ptr(bad_groups), _stream(packed.device)))
     return out

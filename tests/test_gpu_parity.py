@@ -122,19 +122,28 @@ def test_quant_edge_rows(sbl):
 
 
 def test_quant_exact_half_boundaries(sbl):
-    """Weights placed exactly at and one ulp around gamma/2 of their row."""
+    """Rows whose scale is known exactly: half the magnitudes v, half 3v, so
+    gamma = 2v and |w| = v sits exactly on gamma/2 (rounds to 0) and 3v on
+    1.5 gamma (rounds to 2, clipped to 1).  Pairs v+u, v-u (u one ulp) keep
+    the mean exact and put weights one ulp either side of the boundary."""
     rows, cols = 8, 256
-    W = synth.latent_weight("gpu/quant/half", rows, cols)
-    g, _ = oracle.row_scale(W)
-    rng = synth.rng("gpu/quant/half/pos")
+    v = np.float32(3 * 2.0 ** -9)
+    up, dn = np.nextafter(v, np.float32(1)), np.nextafter(v, np.float32(0))
+    assert np.float64(up) - v == v - np.float64(dn)
+    rng = synth.rng("gpu/quant/exact-half")
+    W = np.empty((rows, cols), np.float32)
     for r in range(rows):
-        h = np.float32(g[r] / np.float32(2))
-        for j in rng.choice(cols, 24, replace=False):
-            W[r, j] = rng.choice([h, np.nextafter(h, np.float32(0)), np.nextafter(h, np.float32(1)), -h])
-    # placing values moved the mean; iterate once more so some stay on the boundary
-    g2, _ = oracle.row_scale(W)
+        mags = np.concatenate([np.full(cols // 2 - 16, v), np.repeat([up, dn], 8),
+                               np.full(cols // 2, np.float32(3) * v)]).astype(np.float32)
+        signs = rng.choice(np.array([-1, 1], np.float32), cols)
+        W[r] = rng.permutation(mags * signs)
+    g_ref, _ = oracle.row_scale(W)
+    assert (g_ref == np.float32(2) * v).all()
     packed, scale, sb = sbl.ternary_quant_pack(dev(W))
     _check_quant(W, None, 0, packed, scale, sb)
+    codes = oracle.unpack_codes(host(packed), cols)
+    assert (codes[np.abs(W) == v] == 0).all() and (codes[np.abs(W) == up] != 0).all()
+    assert (codes[np.abs(W) == dn] == 0).all() and (np.abs(codes[np.abs(W) == 3 * v]) == 1).all()
 
 
 def test_grouped_refresh(sbl):
@@ -148,9 +157,9 @@ def test_grouped_refresh(sbl):
                          scale=torch.empty(r, dtype=torch.float32, device=DEV),
                          scale_bf16=torch.empty(r, dtype=torch.int16, device=DEV)))
         refs.append(W)
-    keep = sbl.nm_mask_quant_pack_grouped(jobs, 3, 4)
+    hostd, devd = sbl.refresh_descs(jobs)
+    sbl.nm_mask_quant_pack_grouped(hostd, devd, len(jobs), 3, 4, 0, DEV)
     torch.cuda.synchronize()
-    del keep
     for W, j in zip(refs, jobs):
         mask = oracle.nm_mask(W, 3, 4)
         assert np.array_equal(host(j["mask"]), mask)
