@@ -87,7 +87,10 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t tokens, int64_t cols, int
   if (need <= 1) SBL_AQ(1);
   else if (need <= 2) SBL_AQ(2);
   else if (need <= 4) SBL_AQ(4);
+  else if (need <= 6) SBL_AQ(6);
   else if (need <= 8) SBL_AQ(8);
+  else if (need <= 10) SBL_AQ(10);
+  else if (need <= 12) SBL_AQ(12);
   else if (need <= 16) SBL_AQ(16);
   else SBL_AQ(0);
 #undef SBL_AQ

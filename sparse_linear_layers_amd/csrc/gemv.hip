@@ -59,7 +59,24 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const int tok = lane & 15;
   const uint8_t* wrow = desc.packed + my_row * (K >> 2);
 
+  // Weight codes of one slab: step s (0..7) is 8 bytes = 32 codes at k
+  // offset s*128 + 32*g of the slab.  The loads of slab n+1 are issued
+  // before slab n is computed, so a wave always has a slab in flight.
+  constexpr int kSteps = kGemvSlab / 128;
+  uint2 w0, w1, w2, w3, w4, w5, w6, w7;
+#define SBL_WLD(s, ks_)                                                                 \
+  w##s = ((ks_) + (s) * 128 + 32 * g < K)                                               \
+             ? *reinterpret_cast<const uint2*>(wrow + (((ks_) + (s) * 128 + 32 * g) >> 2)) \
+             : make_uint2(0u, 0u);
+#define SBL_WLOAD(ks_)                                                                  \
+  {                                                                                     \
+    SBL_WLD(0, ks_) SBL_WLD(1, ks_) SBL_WLD(2, ks_) SBL_WLD(3, ks_)                     \
+    SBL_WLD(4, ks_) SBL_WLD(5, ks_) SBL_WLD(6, ks_) SBL_WLD(7, ks_)                     \
+  }
+  static_assert(kSteps == 8, "eight steps per slab");
+
   v4i acc = {0, 0, 0, 0};
+  SBL_WLOAD((int64_t)0);
   for (int64_t ks = 0; ks < K; ks += kGemvSlab) {
     const int width = (int)min<int64_t>(kGemvSlab, K - ks);  // multiple of 64
     __syncthreads();
@@ -74,16 +91,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       *reinterpret_cast<uint4*>(xs + t * kGemvLdsStride + 16 * q) = make_uint4(o[0], o[1], o[2], o[3]);
     }
     __syncthreads();
-    const int steps = (width + 127) >> 7;
-    for (int s = 0; s < steps; ++s) {
+    const uint2 wv[kSteps] = {w0, w1, w2, w3, w4, w5, w6, w7};
+    if (ks + kGemvSlab < K) SBL_WLOAD(ks + kGemvSlab);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
       const int kin = s * 128 + 32 * g;  // k offset inside the slab
-      uint2 w = make_uint2(0u, 0u);
-      if (kin < width) w = *reinterpret_cast<const uint2*>(wrow + ((ks + kin) >> 2));
-      const uint32_t wv[2] = {w.x, w.y};
+      if (s * 128 >= width) break;       // uniform: whole steps past the slab end
+      const uint32_t wd[2] = {wv[s].x, wv[s].y};
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         uint32_t e[4];
-        expand16_strided(wv[i], e);
+        expand16_strided(wd[i], e);
         const v4i av = {(int)e[0], (int)e[1], (int)e[2], (int)e[3]};
         v4i bv = {0, 0, 0, 0};
         if (tok < T && kin < width) bv = *reinterpret_cast<const v4i*>(xs + tok * kGemvLdsStride + kin + 16 * i);
@@ -91,6 +109,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       }
     }
   }
+#undef SBL_WLD
+#undef SBL_WLOAD
   // lane holds C[row = 4*(lane/16) + r][token = lane%16]
   if (tok < T) {
     const float bt = __fdiv_rn(desc.beta[tok], 127.0f);

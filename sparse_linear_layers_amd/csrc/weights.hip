@@ -261,6 +261,7 @@ struct GroupedRefreshArgs {
   const sbl_refresh_desc* descs;
   int count;
   int block_start[kMaxGroupedRefresh + 1];
+  int descs_idx[kMaxGroupedRefresh];  // index into descs of each entry
 };
 
 template <int CPL, int MODE>
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(256) void quant_pack_grouped_kernel(GroupedRefreshA
     const int mid = (lo + hi + 1) >> 1;
     if (args.block_start[mid] <= b) lo = mid; else hi = mid - 1;
   }
-  const sbl_refresh_desc d = args.descs[lo];
+  const sbl_refresh_desc d = args.descs[args.descs_idx[lo]];
   const int64_t row = (int64_t)(b - args.block_start[lo]) * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= d.rows) return;
   RowJob job{d.W, nullptr, d.mask_bits, d.packed, d.row_scale, d.row_scale_bf16, d.rows, d.cols};
@@ -282,14 +283,12 @@ __global__ __launch_bounds__(256) void quant_pack_grouped_kernel(GroupedRefreshA
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
+// Register footprint class of a row: 4-column chunks each lane holds.
 static int chunks_per_lane(int64_t cols) {
   const int64_t need = (cols / 4 + kWave - 1) / kWave;
-  if (need <= 1) return 1;
-  if (need <= 2) return 2;
-  if (need <= 4) return 4;
-  if (need <= 8) return 8;
-  if (need <= 16) return 16;
-  if (need <= 32) return 32;
+  constexpr int kClasses[] = {1, 2, 4, 8, 12, 16, 20, 24, 28, 32};
+  for (int c : kClasses)
+    if (need <= c) return c;
   return 0;  // long-row path
 }
 
@@ -315,7 +314,8 @@ static void launch_row(int cpl, dim3 grid, hipStream_t stream, const RowJob& job
     hipLaunchKernelGGL((quant_pack_kernel<C, MODE>), grid, dim3(256), 0, stream, job, n, \
                        from_masked);                                                       \
     break;
-    SBL_CASE(1) SBL_CASE(2) SBL_CASE(4) SBL_CASE(8) SBL_CASE(16) SBL_CASE(32) SBL_CASE(0)
+    SBL_CASE(1) SBL_CASE(2) SBL_CASE(4) SBL_CASE(8) SBL_CASE(12) SBL_CASE(16) SBL_CASE(20)
+    SBL_CASE(24) SBL_CASE(28) SBL_CASE(32) SBL_CASE(0)
 #undef SBL_CASE
   }
 }
@@ -346,7 +346,8 @@ static void launch_grouped(int cpl, dim3 grid, hipStream_t stream, const Grouped
     hipLaunchKernelGGL((quant_pack_grouped_kernel<C, MODE>), grid, dim3(256), 0, stream, a, n, \
                        fm);                                                                      \
     break;
-    SBL_CASE(1) SBL_CASE(2) SBL_CASE(4) SBL_CASE(8) SBL_CASE(16) SBL_CASE(32) SBL_CASE(0)
+    SBL_CASE(1) SBL_CASE(2) SBL_CASE(4) SBL_CASE(8) SBL_CASE(12) SBL_CASE(16) SBL_CASE(20)
+    SBL_CASE(24) SBL_CASE(28) SBL_CASE(32) SBL_CASE(0)
 #undef SBL_CASE
   }
 }
@@ -354,33 +355,47 @@ static void launch_grouped(int cpl, dim3 grid, hipStream_t stream, const Grouped
 hipError_t launch_quant_pack_grouped(const sbl_refresh_desc* host, const sbl_refresh_desc* dev,
                                      int count, int n, int m, unsigned flags,
                                      hipStream_t stream) {
-  // One launch per run of descriptors that fits the argument block; every
-  // descriptor of one launch uses the chunks-per-lane of its widest row.
-  for (int first = 0; first < count;) {
-    const int last = std::min(count, first + kMaxGroupedRefresh);
+  // One launch per register-footprint class (chunks per lane), each over
+  // the descriptors of that class, so a narrow row never carries the
+  // registers of the widest; the block offsets of a launch travel in its
+  // argument block (at most kMaxGroupedRefresh descriptors per launch).
+  const int fm = (flags & SBL_SCALE_FROM_MASKED) ? 1 : 0;
+  constexpr int kClasses[] = {1, 2, 4, 8, 12, 16, 20, 24, 28, 32, 0};
+  for (int cls : kClasses) {
     GroupedRefreshArgs a;
-    a.descs = dev + first;
-    a.count = last - first;
+    a.descs = dev;
+    int cnt = 0;
     int64_t blocks = 0;
-    int64_t max_cols = 0;
-    for (int d = first; d < last; ++d) {
-      a.block_start[d - first] = (int)blocks;
+    auto flush = [&]() -> hipError_t {
+      if (cnt == 0) return hipSuccess;
+      a.count = cnt;
+      a.block_start[cnt] = (int)blocks;
+      if (blocks > 0) {
+        const dim3 grid((unsigned)blocks);
+        if (m == 4)
+          launch_grouped<1>(cls, grid, stream, a, n, fm);
+        else
+          launch_grouped<2>(cls, grid, stream, a, n, fm);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      cnt = 0;
+      blocks = 0;
+      return hipSuccess;
+    };
+    for (int d = 0; d < count; ++d) {
+      if (chunks_per_lane(host[d].cols) != cls || host[d].rows == 0) continue;
+      if (cnt == kMaxGroupedRefresh) {
+        hipError_t e = flush();
+        if (e != hipSuccess) return e;
+      }
+      a.descs_idx[cnt] = d;
+      a.block_start[cnt] = (int)blocks;
       blocks += (host[d].rows + kRowsPerBlock - 1) / kRowsPerBlock;
-      max_cols = std::max(max_cols, host[d].cols);
+      ++cnt;
     }
-    a.block_start[last - first] = (int)blocks;
-    if (blocks > 0) {
-      const int cpl = chunks_per_lane(max_cols);
-      const int fm = (flags & SBL_SCALE_FROM_MASKED) ? 1 : 0;
-      const dim3 grid((unsigned)blocks);
-      if (m == 4)
-        launch_grouped<1>(cpl, grid, stream, a, n, fm);
-      else
-        launch_grouped<2>(cpl, grid, stream, a, n, fm);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    first = last;
+    hipError_t e = flush();
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
