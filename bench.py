@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target host time of the oracle sample")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run 4 device copies of MIB MiB (reference for the HBM byte "
+                        "counters under rocprofv3) and exit")
     return p.parse_args()
 
 
@@ -118,6 +121,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.calibrate_copy} MiB x 4")
+        return
 
     import sparse_linear_layers_amd as sbl
     from sparse_linear_layers_amd import synth
