@@ -85,17 +85,15 @@ hipError_t launch_sparse24_compress(const uint8_t* packed, int64_t N, int64_t K,
 }
 
 // ---------------------------------------------------------------------------
-// smfmac GEMM: same block structure as the dense kernel, one 64-wide k step
-// per stage and one smfmac per 32x32 tile pair per stage.
+// smfmac GEMM: the structure of the dense product kernel (persistent blocks
+// over XCD-contiguous tile ranges, flattened (tile, k-step) loop, two
+// register stages, double-buffered LDS), one 64-wide k step per stage and
+// one smfmac per 32x32 tile pair per step.
 // ---------------------------------------------------------------------------
-constexpr int kSpBK = 64;
-constexpr int kSpAStride = 48;  // bytes per staged weight row: 2 x 16 values + pad
-constexpr int kSpBStride = 80;  // bytes per staged token row: 64 + pad
-
 struct Sp24Args {
   const int8_t* xq;
   const float* beta;
-  const uint2* sp;
+  const uint8_t* sp;
   const void* scale;
   float* y;
   int32_t* acc;
@@ -103,87 +101,91 @@ struct Sp24Args {
   int scale_bf16;
   int vec_store;
   int tiles_o;
-  int nblocks;
+  int ntiles;
 };
 
-__device__ __forceinline__ int xcd_swizzle24(int b, int nblocks) {
+struct SpTileRange {
+  int first, step, end;
+};
+__device__ __forceinline__ SpTileRange sp_tile_range(int b, int G, int ntiles) {
   constexpr int kXcd = 8;
-  const int per = nblocks / kXcd;
-  if (b >= per * kXcd) return b;
-  return (b % kXcd) * per + b / kXcd;
+  const int X = G < kXcd ? G : kXcd;
+  const int x = b % X;
+  SpTileRange r;
+  r.step = (G - x + X - 1) / X;
+  r.first = (int)((int64_t)ntiles * x / X) + b / X;
+  r.end = (int)((int64_t)ntiles * (x + 1) / X);
+  return r;
 }
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_sp24_kernel(Sp24Args a) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int WTM = BM / WM, WTN = BN / WN;
+template <int BM, int BN>
+__global__ __launch_bounds__(256, 2) void gemm_sp24_kernel(Sp24Args a) {
+  constexpr int AST = 48;                      // bytes per staged weight row: 2 x 16 values + pad
+  constexpr int BST = 80;                      // bytes per staged token row: 64 + pad
+  constexpr int NT = 256;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int A_PER = (BM + NT - 1) / NT;  // weight rows per thread (16 B each)
   constexpr int B_PER = BN * 4 / NT;
-  static_assert(BN * 4 % NT == 0, "B tile split");
+  static_assert(BM <= NT && B_PER == 2, "tile split");
 
-  __shared__ __attribute__((aligned(16))) int8_t sAv[BM * kSpAStride];
-  __shared__ uint32_t sAi[BM * 2];
-  __shared__ __attribute__((aligned(16))) int8_t sB[BN * kSpBStride];
+  __shared__ __attribute__((aligned(16))) int8_t sAv[2][BM * AST];
+  __shared__ uint32_t sAi[2][BM * 2];
+  __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * BST];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave % WM, wn = wave / WM;
-  const int tile = xcd_swizzle24(blockIdx.x, a.nblocks);
-  const int64_t o0 = (int64_t)(tile % a.tiles_o) * BM;
-  const int64_t t0 = (int64_t)(tile / a.tiles_o) * BN;
+  const int wm = wave & 1, wn = wave >> 1;
   const int64_t K = a.K;
-  const int64_t kblocks = K >> 6;
+  const int64_t rowbytes = K >> 2;  // image bytes per weight row (16 per 64-wide k block)
+  const int KT = (int)(K >> 6);
 
-  const uint4* a_src[A_PER];
-  int a_row[A_PER];
-  bool a_on[A_PER];
-#pragma unroll
-  for (int i = 0; i < A_PER; ++i) {
-    const int r = tid + i * NT;
-    a_on[i] = r < BM;
-    a_row[i] = r;
-    const int64_t o = min(o0 + r, a.N - 1);
-    a_src[i] = reinterpret_cast<const uint4*>(a.sp + o * kblocks * 2);
+  const SpTileRange tr = sp_tile_range(blockIdx.x, gridDim.x, a.ntiles);
+  if (tr.first >= tr.end) return;
+  const int total = ((tr.end - tr.first + tr.step - 1) / tr.step) * KT;
+  int ld_tile = tr.first, ld_kt = 0;
+  int64_t ld_o0 = (int64_t)(ld_tile % a.tiles_o) * BM, ld_t0 = (int64_t)(ld_tile / a.tiles_o) * BN;
+  int cp_tile = tr.first, cp_kt = 0;
+
+  const bool a_on = tid < BM;
+  const int a_row = tid;
+  const int b_row0 = tid >> 2, b_part = (tid & 3) * 16;
+
+  uint4 ra_0, rb0_0, rb1_0;
+  uint4 ra_1, rb0_1, rb1_1;
+
+#define SBL_LOAD(S)                                                                     \
+  {                                                                                     \
+    if (a_on) {                                                                         \
+      const int r_ = (int)min((int64_t)a_row, a.N - 1 - ld_o0);                         \
+      ra_##S = *reinterpret_cast<const uint4*>(a.sp + (ld_o0 + r_) * rowbytes + ld_kt * 16); \
+    }                                                                                   \
+    const int8_t* xb_ = a.xq + ld_t0 * K + ld_kt * 64 + b_part;                         \
+    const int last_ = (int)min((int64_t)(BN - 1), a.T - 1 - ld_t0);                     \
+    rb0_##S = *reinterpret_cast<const uint4*>(xb_ + min(b_row0, last_) * (int)K);       \
+    rb1_##S = *reinterpret_cast<const uint4*>(xb_ + min(b_row0 + 64, last_) * (int)K);  \
+    if (++ld_kt == KT) {                                                                \
+      ld_kt = 0;                                                                        \
+      ld_tile += tr.step;                                                               \
+      ld_o0 = (int64_t)(ld_tile % a.tiles_o) * BM;                                      \
+      ld_t0 = (int64_t)(ld_tile / a.tiles_o) * BN;                                      \
+    }                                                                                   \
   }
-  const int8_t* b_src[B_PER];
-  int b_dst[B_PER];
-#pragma unroll
-  for (int i = 0; i < B_PER; ++i) {
-    const int ci = tid + i * NT;
-    const int r = ci >> 2, part = ci & 3;
-    const int64_t t = min(t0 + r, a.T - 1);
-    b_src[i] = a.xq + t * K + part * 16;
-    b_dst[i] = r * kSpBStride + part * 16;
+
+#define SBL_STORE(S, buf)                                                               \
+  {                                                                                     \
+    if (a_on) {                                                                         \
+      uint32_t e_[4];                                                                   \
+      expand16_strided(ra_##S.x, e_);                                                   \
+      *reinterpret_cast<uint4*>(sAv[buf] + a_row * AST) = make_uint4(e_[0], e_[1], e_[2], e_[3]); \
+      expand16_strided(ra_##S.z, e_);                                                   \
+      *reinterpret_cast<uint4*>(sAv[buf] + a_row * AST + 16) = make_uint4(e_[0], e_[1], e_[2], e_[3]); \
+      *reinterpret_cast<uint2*>(&sAi[buf][a_row * 2]) = make_uint2(ra_##S.y, ra_##S.w);  \
+    }                                                                                   \
+    int8_t* s_ = sB[buf] + b_row0 * BST + b_part;                                       \
+    *reinterpret_cast<uint4*>(s_) = rb0_##S;                                            \
+    *reinterpret_cast<uint4*>(s_ + 64 * BST) = rb1_##S;                                 \
   }
-  uint4 a_reg[A_PER];
-  uint4 b_reg[B_PER];
-  auto load_tile = [&](int64_t kt) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i)
-      if (a_on[i]) a_reg[i] = a_src[i][kt];
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i)
-      b_reg[i] = *reinterpret_cast<const uint4*>(b_src[i] + kt * kSpBK);
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      if (!a_on[i]) continue;
-      const uint32_t vw[2] = {a_reg[i].x, a_reg[i].z};
-      const uint32_t iw[2] = {a_reg[i].y, a_reg[i].w};
-#pragma unroll
-      for (int G = 0; G < 2; ++G) {
-        uint32_t e[4];
-        expand16_strided(vw[G], e);
-        *reinterpret_cast<uint4*>(sAv + a_row[i] * kSpAStride + 16 * G) = make_uint4(e[0], e[1], e[2], e[3]);
-        sAi[a_row[i] * 2 + G] = iw[G];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) *reinterpret_cast<uint4*>(sB + b_dst[i]) = b_reg[i];
-  };
 
   v16i acc[TM][TN];
 #pragma unroll
@@ -191,12 +193,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_sp24_kernel(Sp24Args a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
 
-  load_tile(0);
-  for (int64_t kt = 0; kt < kblocks; ++kt) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < kblocks) load_tile(kt + 1);
+  auto compute = [&](int buf) {
     const int G = lane >> 5;
     v4i af[TM];
     int ai[TM];
@@ -204,12 +201,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_sp24_kernel(Sp24Args a) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = wm * WTM + i * 32 + (lane & 31);
-      af[i] = *reinterpret_cast<const v4i*>(sAv + r * kSpAStride + 16 * G);
-      ai[i] = (int)sAi[r * 2 + G];
+      af[i] = *reinterpret_cast<const v4i*>(sAv[buf] + r * AST + 16 * G);
+      ai[i] = (int)sAi[buf][r * 2 + G];
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int8_t* p = sB + (wn * WTN + j * 32 + (lane & 31)) * kSpBStride + 32 * G;
+      const int8_t* p = sB[buf] + (wn * WTN + j * 32 + (lane & 31)) * BST + 32 * G;
       const v4i lo = *reinterpret_cast<const v4i*>(p);
       const v4i hi = *reinterpret_cast<const v4i*>(p + 16);
       bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -219,62 +216,110 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_sp24_kernel(Sp24Args a) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(af[i], bf[j], acc[i][j], ai[i], 0, 0);
-  }
+  };
 
+  auto epilogue = [&]() {
+    const int64_t o0 = (int64_t)(cp_tile % a.tiles_o) * BM;
+    const int64_t t0 = (int64_t)(cp_tile / a.tiles_o) * BN;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int64_t t = t0 + wn * WTN + j * 32 + (lane & 31);
-    if (t >= a.T) continue;
-    const float bt = __fdiv_rn(a.beta[t], 127.0f);
+    for (int jn = 0; jn < TN; ++jn) {
+      const int64_t t = t0 + wn * WTN + jn * 32 + (lane & 31);
+      const bool t_ok = t < a.T;
+      const float bt = __fdiv_rn(a.beta[t_ok ? t : 0], 127.0f);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+      for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int64_t o = o0 + wm * WTM + i * 32 + 8 * r4 + 4 * (lane >> 5);
-        if (o >= a.N) continue;
-        int32_t c[4];
-        float yv[4];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int64_t o = o0 + wm * WTM + i * 32 + 8 * r4 + 4 * (lane >> 5);
+          if (!t_ok || o >= a.N) continue;
+          int32_t c[4];
+          float yv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          c[e] = acc[i][j][4 * r4 + e];
-          const int64_t oe = min(o + e, a.N - 1);
-          yv[e] = ((float)c[e] * bt) * load_scale(a.scale, a.scale_bf16, oe);
-        }
-        float* yp = a.y + t * a.N + o;
-        int32_t* ap = a.acc ? a.acc + t * a.N + o : nullptr;
-        if (a.vec_store) {
-          *reinterpret_cast<float4*>(yp) = make_float4(yv[0], yv[1], yv[2], yv[3]);
-          if (ap) *reinterpret_cast<int4*>(ap) = make_int4(c[0], c[1], c[2], c[3]);
-        } else {
+          for (int e = 0; e < 4; ++e) {
+            c[e] = acc[i][jn][4 * r4 + e];
+            const int64_t oe = min(o + e, a.N - 1);
+            yv[e] = ((float)c[e] * bt) * load_scale(a.scale, a.scale_bf16, oe);
+          }
+          float* yp = a.y + t * a.N + o;
+          int32_t* ap = a.acc ? a.acc + t * a.N + o : nullptr;
+          if (a.vec_store) {
+            *reinterpret_cast<float4*>(yp) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+            if (ap) *reinterpret_cast<int4*>(ap) = make_int4(c[0], c[1], c[2], c[3]);
+          } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (o + e < a.N) {
-              yp[e] = yv[e];
-              if (ap) ap[e] = c[e];
-            }
+            for (int e = 0; e < 4; ++e)
+              if (o + e < a.N) {
+                yp[e] = yv[e];
+                if (ap) ap[e] = c[e];
+              }
+          }
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn) acc[i][jn] = v16i{};
+  };
+
+#define SBL_ITER(S)                                                                     \
+  {                                                                                     \
+    compute(it & 1);                                                                    \
+    if (it + 1 < total) SBL_STORE(S, (it + 1) & 1);                                     \
+    if (it + 3 < total) SBL_LOAD(S);                                                    \
+    if (++cp_kt == KT) {                                                                \
+      cp_kt = 0;                                                                        \
+      epilogue();                                                                       \
+      cp_tile += tr.step;                                                               \
+    }                                                                                   \
+    __syncthreads();                                                                    \
+    ++it;                                                                               \
   }
+
+  SBL_LOAD(0);
+  SBL_STORE(0, 0);
+  if (total > 1) SBL_LOAD(1);
+  if (total > 2) SBL_LOAD(0);
+  __syncthreads();
+  int it = 0;
+  while (it < total) {
+    SBL_ITER(1);
+    if (it >= total) break;
+    SBL_ITER(0);
+  }
+#undef SBL_ITER
+#undef SBL_LOAD
+#undef SBL_STORE
 }
 
-template <int BM, int BN, int WM, int WN>
-static hipError_t launch_sp_cfg(Sp24Args a, hipStream_t stream) {
-  a.tiles_o = (int)((a.N + BM - 1) / BM);
-  const int64_t nb = (int64_t)a.tiles_o * ((a.T + BN - 1) / BN);
-  a.nblocks = (int)nb;
-  hipLaunchKernelGGL((gemm_sp24_kernel<BM, BN, WM, WN>), dim3((unsigned)nb), dim3(WM * WN * 64),
-                     0, stream, a);
-  return hipGetLastError();
+static int sp_num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
 }
 
 hipError_t launch_gemm_sparse24(const int8_t* xq, const float* beta, const void* sp,
                                 const void* scale, int scale_bf16, int64_t T, int64_t K, int64_t N,
                                 float* y, int32_t* acc, hipStream_t stream) {
-  Sp24Args a{xq, beta, reinterpret_cast<const uint2*>(sp), scale, y, acc, T, K, N, scale_bf16,
+  constexpr int BM = 128, BN = 128;
+  Sp24Args a{xq, beta, reinterpret_cast<const uint8_t*>(sp), scale, y, acc, T, K, N, scale_bf16,
              (N % 4) == 0, 0, 0};
-  if (N >= 1024 && (N % 256 == 0 || N > 2048)) return launch_sp_cfg<256, 128, 2, 2>(a, stream);
-  return launch_sp_cfg<128, 128, 2, 2>(a, stream);
+  a.tiles_o = (int)((N + BM - 1) / BM);
+  a.ntiles = (int)((int64_t)a.tiles_o * ((T + BN - 1) / BN));
+  int occ = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_sp24_kernel<BM, BN>, 256, 0) !=
+          hipSuccess || occ < 1)
+    occ = 1;
+  const int grid = (int)std::min<int64_t>(a.ntiles, (int64_t)occ * sp_num_cus());
+  hipLaunchKernelGGL((gemm_sp24_kernel<BM, BN>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace sbl
