@@ -8,8 +8,8 @@
 // The stream of packed codes (1/4 B per weight) is the whole cost, so the
 // kernel is built around reading it once at full HBM rate with as little
 // ALU per byte as possible:
-//  * A wave owns 16 weight rows; lane l reads 8 bytes (32 codes) of row
-//    l%16 at k offset 32*(l/16) of each 128-code step.  The v_mfma
+//  * A wave owns 16 weight rows; lane l reads 16 bytes (64 codes) of row
+//    l%16 at k offset 64*(l/16) of each 256-code step.  The v_mfma
 //    i32_16x16x64_i8 then does the whole k reduction in the matrix core:
 //    no cross-lane reduction, and the token count (1..16) rides in the
 //    MFMA's N dimension for free.
@@ -41,39 +41,42 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int b = blockIdx.x;
+  // descriptor of this block: the last d with block_start[d] <= b, found
+  // with one round of parallel reads and a ballot count (one memory latency
+  // instead of a dependent binary search)
   int d = 0;
   if (a.descs) {
-    int lo = 0, hi = a.count - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.block_start[mid] <= b) lo = mid; else hi = mid - 1;
+    int cnt = 0;
+    for (int j = 0; j < a.count; j += kWave) {
+      const int idx = j + lane;
+      const bool le = idx < a.count && a.block_start[idx] <= b;
+      cnt += __popcll(__ballot(le));
     }
-    d = lo;
+    d = cnt - 1;
   }
   const sbl_gemv_desc desc = a.descs ? a.descs[d] : a.single;
   const int64_t K = desc.K, N = desc.N;
   const int T = a.T;
   const int64_t row0 = (int64_t)(b - a.block_start[d]) * kGemvRowsPerBlock + wave * kGemvRowsPerWave;
-  const int64_t my_row = min(row0 + (lane & 15), N - 1);
   const int g = lane >> 4;  // k group within a step
   const int tok = lane & 15;
-  const uint8_t* wrow = desc.packed + my_row * (K >> 2);
+  const uint8_t* wrow = desc.packed + min(row0 + (lane & 15), N - 1) * (K >> 2);
+  const int xrow = min(tok, T - 1) * kGemvLdsStride;  // LDS row this lane's B operand reads
 
-  // Weight codes of one slab: step s (0..7) is 8 bytes = 32 codes at k
-  // offset s*128 + 32*g of the slab.  The loads of slab n+1 are issued
-  // before slab n is computed, so a wave always has a slab in flight.
-  constexpr int kSteps = kGemvSlab / 128;
-  uint2 w0, w1, w2, w3, w4, w5, w6, w7;
+  // Weight codes of one slab: super-step s (0..3) is 16 bytes = 64 codes of
+  // row lane%16 at k offset s*256 + 64*g of the slab (4 lanes cover 64
+  // contiguous bytes of a row).  Its dword i feeds MFMA i, whose lane group g
+  // then covers k = s*256 + 64*g + 16*i .. +16 on both operands.  The loads
+  // of slab n+1 are issued before slab n is computed.
+  constexpr int kSteps = kGemvSlab / 256;
+  uint4 w0, w1, w2, w3;
 #define SBL_WLD(s, ks_)                                                                 \
-  w##s = ((ks_) + (s) * 128 + 32 * g < K)                                               \
-             ? *reinterpret_cast<const uint2*>(wrow + (((ks_) + (s) * 128 + 32 * g) >> 2)) \
-             : make_uint2(0u, 0u);
+  w##s = ((ks_) + (s) * 256 + 64 * g < K)                                               \
+             ? *reinterpret_cast<const uint4*>(wrow + (((ks_) + (s) * 256 + 64 * g) >> 2)) \
+             : make_uint4(0u, 0u, 0u, 0u);
 #define SBL_WLOAD(ks_)                                                                  \
-  {                                                                                     \
-    SBL_WLD(0, ks_) SBL_WLD(1, ks_) SBL_WLD(2, ks_) SBL_WLD(3, ks_)                     \
-    SBL_WLD(4, ks_) SBL_WLD(5, ks_) SBL_WLD(6, ks_) SBL_WLD(7, ks_)                     \
-  }
-  static_assert(kSteps == 8, "eight steps per slab");
+  { SBL_WLD(0, ks_) SBL_WLD(1, ks_) SBL_WLD(2, ks_) SBL_WLD(3, ks_) }
+  static_assert(kSteps == 4, "four super-steps per slab");
 
   v4i acc = {0, 0, 0, 0};
   SBL_WLOAD((int64_t)0);
@@ -82,29 +85,30 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     __syncthreads();
     // stage x~[0:T, ks:ks+width] with each 16-byte chunk byte-transposed
     const int cpt = width >> 4;
-    for (int c = tid; c < T * cpt; c += 256) {
-      const int t = c / cpt, q = c - t * cpt;
-      const uint4 v = *reinterpret_cast<const uint4*>(desc.xq + (int64_t)t * K + ks + 16 * q);
-      const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o[4];
-      transpose4x4(in, o);
-      *reinterpret_cast<uint4*>(xs + t * kGemvLdsStride + 16 * q) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+    for (int t = 0; t < T; ++t)
+      for (int q = tid; q < cpt; q += 256) {
+        const uint4 v = *reinterpret_cast<const uint4*>(desc.xq + (int64_t)t * K + ks + 16 * q);
+        const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+        transpose4x4(in, o);
+        *reinterpret_cast<uint4*>(xs + t * kGemvLdsStride + 16 * q) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
     __syncthreads();
-    const uint2 wv[kSteps] = {w0, w1, w2, w3, w4, w5, w6, w7};
+    const uint4 wv[kSteps] = {w0, w1, w2, w3};
     if (ks + kGemvSlab < K) SBL_WLOAD(ks + kGemvSlab);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int kin = s * 128 + 32 * g;  // k offset inside the slab
-      if (s * 128 >= width) break;       // uniform: whole steps past the slab end
-      const uint32_t wd[2] = {wv[s].x, wv[s].y};
+      if (s * 256 >= width) break;  // uniform: whole super-steps past the slab end
+      const int kin = s * 256 + 64 * g;  // k offset of this lane group inside the slab
+      const uint32_t wd[4] = {wv[s].x, wv[s].y, wv[s].z, wv[s].w};
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 4; ++i) {
         uint32_t e[4];
         expand16_strided(wd[i], e);
         const v4i av = {(int)e[0], (int)e[1], (int)e[2], (int)e[3]};
-        v4i bv = {0, 0, 0, 0};
-        if (tok < T && kin < width) bv = *reinterpret_cast<const v4i*>(xs + tok * kGemvLdsStride + kin + 16 * i);
+        // lanes of token slots >= T read a real row (their output columns
+        // are never stored); past the k tail the codes are zero
+        const v4i bv = *reinterpret_cast<const v4i*>(xs + xrow + kin + 16 * i);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
       }
     }
