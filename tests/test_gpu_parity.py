@@ -239,6 +239,25 @@ def test_gemm_extreme_operands(sbl):
     assert_y_close(host(y), oracle.dequant(acc_ref, beta, g))
 
 
+@pytest.mark.parametrize("T,K,N,bf16_scale", [(16400, 320, 1000, False), (16400, 192, 1002, True),
+                                                (8292, 896, 4864, False), (16385, 4864, 896, True)])
+def test_gemm_large_tiles(sbl, T, K, N, bf16_scale):
+    """Sizes that take the 256 x 256-tile kernel (at least one tile per
+    CU): ragged token and row edges, K % 128 == 64, N % 4 != 0 (scalar
+    stores).  acc and y compared in full on sampled token rows that cover
+    whole tiles at the start and the ragged edge at the end."""
+    o = _operands(f"gpu/gemm_big/{T}x{K}x{N}", T, K, N)
+    scale = dev(o["gb"]) if bf16_scale else dev(o["g"])
+    y, acc = sbl.sparse_bitlinear_gemm(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), scale,
+                                       want_acc=True)
+    rnd = synth.rng(f"gpu/gemm_big/{T}x{K}x{N}/rows").choice(T, 64, replace=False)
+    rows = np.unique(np.concatenate([np.arange(300), np.arange(T - 300, T), rnd]))
+    acc_ref = oracle.gemm_acc(o["xq"][rows], o["codes"])
+    assert np.array_equal(host(acc)[rows], acc_ref)
+    g_used = oracle.bf16_bits_to_float(o["gb"]) if bf16_scale else o["g"]
+    assert_y_close(host(y)[rows], oracle.dequant(acc_ref, o["beta"][rows], g_used))
+
+
 @pytest.mark.parametrize("name,N,K", [("q", 896, 896), ("k", 128, 896), ("gate", 4864, 896),
                                       ("down", 896, 4864), ("wide_up", 7168, 2048),
                                       ("wide_down", 2048, 7168)])
