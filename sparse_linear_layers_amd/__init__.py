@@ -126,6 +126,15 @@ def _need(t, dtype, name, ndim=None):
     return t
 
 
+def _shape(t, shape, dtype, name):
+    """A caller-provided tensor must match the size the kernels write or
+    read exactly: the C ABI only sees its pointer."""
+    _need(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 _BF16_BITS = (torch.bfloat16, torch.int16, torch.uint16) if hasattr(torch, "uint16") \
     else (torch.bfloat16, torch.int16)
 
@@ -166,6 +175,12 @@ def nm_mask_quant_pack(W: torch.Tensor, n: int, m: int, flags: int = 0,
     dev = W.device
     if out is not None:
         mask, packed, scale, sb = out
+        if mask is not None:
+            _shape(mask, (rows * cols // 8,), torch.uint8, "mask")
+        _shape(packed, (rows, cols // 4), torch.uint8, "packed")
+        _shape(scale, (rows,), torch.float32, "scale")
+        if sb is not None:
+            _shape(sb, (rows,), _BF16_BITS, "scale_bf16")
     else:
         mask = torch.empty(rows * cols // 8, dtype=torch.uint8, device=dev) if want_mask else None
         packed = torch.empty((rows, cols // 4), dtype=torch.uint8, device=dev)
@@ -193,6 +208,13 @@ def refresh_descs(jobs):
     for j in jobs:
         W = _need(j["W"], torch.float32, "W", 2)
         mask, sb = j.get("mask"), j.get("scale_bf16")
+        rows, cols = W.shape
+        _shape(j["packed"], (rows, cols // 4), torch.uint8, "packed")
+        _shape(j["scale"], (rows,), torch.float32, "scale")
+        if mask is not None:
+            _shape(mask, (rows * cols // 8,), torch.uint8, "mask")
+        if sb is not None:
+            _shape(sb, (rows,), _BF16_BITS, "scale_bf16")
         ds.append(RefreshDesc(W.data_ptr(), mask.data_ptr() if mask is not None else None,
                               j["packed"].data_ptr(), j["scale"].data_ptr(),
                               sb.data_ptr() if sb is not None else None,
@@ -218,6 +240,8 @@ def act_quant_i8(x: torch.Tensor, xq: torch.Tensor | None = None,
         xq = torch.empty((T, K), dtype=torch.int8, device=x.device)
     if beta is None:
         beta = torch.empty(T, dtype=torch.float32, device=x.device)
+    _shape(xq, (T, K), torch.int8, "xq")
+    _shape(beta, (T,), torch.float32, "beta")
     _check("act_quant_i8", load().act_quant_i8(_ptr(x), T, K, _ptr(xq), _ptr(beta),
                                                _stream(x.device)))
     return xq, beta
@@ -243,9 +267,12 @@ def sparse_bitlinear_gemm(xq, beta, packed, scale, want_acc: bool = False,
     N = packed.shape[0]
     if packed.shape[1] * 4 != K:
         raise ValueError("packed must be [N, K/4]")
+    _shape(beta, (T,), torch.float32, "beta")
+    _shape(scale, (N,), None, "scale")
     dev = xq.device
     if y is None:
         y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    _shape(y, (T, N), torch.float32, "y")
     acc = torch.empty((T, N), dtype=torch.int32, device=dev) if want_acc else None
     _check("sparse_bitlinear_gemm", load().sparse_bitlinear_gemm(
         _ptr(xq), _ptr(beta), _ptr(packed), _ptr(scale), _scale_dtype(scale), T, K, N,
@@ -276,9 +303,14 @@ def sparse_bitlinear_gemm_sparse24(xq, beta, sp24, N: int, scale, want_acc: bool
     _need(sp24, torch.uint8, "sparse24")
     _need(scale, None, "scale", 1)
     T, K = xq.shape
+    _shape(beta, (T,), torch.float32, "beta")
+    _shape(scale, (N,), None, "scale")
+    if sp24.numel() < sparse24_bytes(N, K):
+        raise ValueError("sparse24: image smaller than sparse24_bytes(N, K)")
     dev = xq.device
     if y is None:
         y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    _shape(y, (T, N), torch.float32, "y")
     acc = torch.empty((T, N), dtype=torch.int32, device=dev) if want_acc else None
     _check("sparse_bitlinear_gemm_sparse24", load().sparse_bitlinear_gemm_sparse24(
         _ptr(xq), _ptr(beta), _ptr(sp24), _ptr(scale), _scale_dtype(scale), T, K, N,
@@ -293,9 +325,14 @@ def sparse_bitlinear_gemv(xq, beta, packed, scale, y: torch.Tensor | None = None
     _need(scale, None, "scale", 1)
     T, K = xq.shape
     N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError("packed must be [N, K/4]")
+    _shape(beta, (T,), torch.float32, "beta")
+    _shape(scale, (N,), None, "scale")
     dev = xq.device
     if y is None:
         y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    _shape(y, (T, N), torch.float32, "y")
     _check("sparse_bitlinear_gemv", load().sparse_bitlinear_gemv(
         _ptr(xq), _ptr(beta), _ptr(packed), _ptr(scale), _scale_dtype(scale), T, K, N,
         _ptr(y), _stream(dev)))
@@ -307,8 +344,19 @@ def gemv_descs(jobs):
     sparse_bitlinear_gemv_grouped from dicts with xq, beta, packed, scale, y."""
     dev = jobs[0]["xq"].device
     ds = []
+    if len({j["xq"].shape[0] for j in jobs}) > 1:
+        raise ValueError("gemv_descs: every job of a grouped launch has the same token count")
     for j in jobs:
         xq, packed, scale = j["xq"], j["packed"], j["scale"]
+        _need(xq, torch.int8, "xq", 2)
+        _need(packed, torch.uint8, "packed", 2)
+        T, K = xq.shape
+        N = packed.shape[0]
+        if packed.shape[1] * 4 != K:
+            raise ValueError("packed must be [N, K/4]")
+        _shape(j["beta"], (T,), torch.float32, "beta")
+        _shape(scale, (N,), None, "scale")
+        _shape(j["y"], (T, N), torch.float32, "y")
         ds.append(GemvDesc(xq.data_ptr(), j["beta"].data_ptr(), packed.data_ptr(),
                            scale.data_ptr(), j["y"].data_ptr(), xq.shape[1], packed.shape[0],
                            _scale_dtype(scale), 0))

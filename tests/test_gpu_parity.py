@@ -242,9 +242,8 @@ def test_gemm_extreme_operands(sbl):
 @pytest.mark.parametrize("T,K,N,bf16_scale", [(16400, 320, 1000, False), (16400, 192, 1002, True),
                                                 (8292, 896, 4864, False), (16385, 4864, 896, True)])
 def test_gemm_large_tiles(sbl, T, K, N, bf16_scale):
-    """Sizes that take the 256 x 256-tile kernel (at least one tile per
-    CU): ragged token and row edges, K % 128 == 64, N % 4 != 0 (scalar
-    stores).  acc and y compared in full on sampled token rows that cover
+    """Sizes that take the large-tile persistent kernel (at least one tile
+    per CU): ragged token and row edges, K % 128 == 64, N % 4 != 0.  acc and y compared in full on sampled token rows that cover
     whole tiles at the start and the ragged edge at the end."""
     o = _operands(f"gpu/gemm_big/{T}x{K}x{N}", T, K, N)
     scale = dev(o["gb"]) if bf16_scale else dev(o["g"])
@@ -256,6 +255,23 @@ def test_gemm_large_tiles(sbl, T, K, N, bf16_scale):
     assert np.array_equal(host(acc)[rows], acc_ref)
     g_used = oracle.bf16_bits_to_float(o["gb"]) if bf16_scale else o["g"]
     assert_y_close(host(y)[rows], oracle.dequant(acc_ref, o["beta"][rows], g_used))
+
+
+@pytest.mark.parametrize("T,K,N", [(16400, 320, 1000), (8193, 896, 896), (300, 896, 200)])
+def test_gemm_stores_stay_in_bounds(sbl, T, K, N):
+    """y (and the int32 hook) sit inside larger buffers filled with a
+    sentinel: rows past T, and the columns past N of a partial feature tile,
+    must never be written."""
+    o = _operands(f"gpu/gemm_guard/{T}x{K}x{N}", T, K, N)
+    pad = 300
+    ybig = torch.full(((T + pad) * N + 64,), float("nan"), dtype=torch.float32, device=DEV)
+    y = ybig[:T * N].view(T, N)
+    y, _ = sbl.sparse_bitlinear_gemm(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), dev(o["g"]), y=y)
+    tail = host(ybig[T * N:])
+    assert np.isnan(tail).all(), "stores past the end of y"
+    rows = np.unique(np.concatenate([np.arange(min(T, 260)), np.arange(max(0, T - 260), T)]))
+    acc_ref = oracle.gemm_acc(o["xq"][rows], o["codes"])
+    assert_y_close(host(y)[rows], oracle.dequant(acc_ref, o["beta"][rows], o["g"]))
 
 
 @pytest.mark.parametrize("name,N,K", [("q", 896, 896), ("k", 128, 896), ("gate", 4864, 896),
@@ -368,6 +384,24 @@ def test_errors_raise(sbl):
         sbl.sparse_bitlinear_gemv(x, torch.ones(20, device=DEV),
                                   torch.zeros((8, 16), dtype=torch.uint8, device=DEV),
                                   torch.ones(8, device=DEV))
+
+
+def test_binding_rejects_mis_sized_buffers(sbl):
+    """The C ABI sees only pointers: the binding checks every buffer it is
+    handed against the sizes the kernels will touch."""
+    xq = torch.zeros((20, 64), dtype=torch.int8, device=DEV)
+    packed = torch.zeros((8, 16), dtype=torch.uint8, device=DEV)
+    ok = dict(beta=torch.ones(20, device=DEV), scale=torch.ones(8, device=DEV))
+    with pytest.raises(ValueError):
+        sbl.sparse_bitlinear_gemm(xq, ok["beta"], packed, ok["scale"],
+                                  y=torch.empty((20, 7), device=DEV))
+    with pytest.raises(ValueError):
+        sbl.sparse_bitlinear_gemm(xq, torch.ones(19, device=DEV), packed, ok["scale"])
+    with pytest.raises(ValueError):
+        sbl.sparse_bitlinear_gemm(xq, ok["beta"], packed, torch.ones(9, device=DEV))
+    with pytest.raises(ValueError):
+        sbl.act_quant_i8(torch.zeros((4, 64), dtype=torch.int16, device=DEV),
+                         torch.empty((4, 63), dtype=torch.int8, device=DEV))
 
 
 def test_repeat_runs_are_bitwise_identical(sbl):
