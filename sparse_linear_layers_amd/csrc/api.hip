@@ -203,7 +203,7 @@ int sparse_bitlinear_gemv_grouped(const sbl_gemv_desc* descs_host, const sbl_gem
                               nullptr))
       return s;
     if (d.reserved != 0) return SBL_ERR_ARG;
-    blocks += (d.N + 63) / 64;
+    blocks += sbl::gemv_blocks(d.N, T);
   }
   if (blocks > INT32_MAX / 2) return SBL_ERR_ARG;
   (void)hipGetLastError();
