@@ -32,6 +32,17 @@ something other than itself; the tests named are under ``tests/``):
                      a power of two leaves x~ unchanged (test_oracle_act.py).
 * ``gemm_acc``       numpy int64 matmul of the unpacked operands; pure Python
                      brute force on tiny shapes (test_oracle_gemm.py).
+* ``rmsnorm_act_quant``  each float step re-derived exactly (exact rational
+                     mean, high-precision decimal square root, exact
+                     rounding) on small rows; a float64 statement of
+                     RMSNorm within float rounding; power-of-two scaling
+                     invariance at eps = 0; zero and constant rows
+                     (test_oracle_next.py).
+* ``mask_stats``     pure-Python bit-by-bit count on random masks; masks
+                     from ``nm_mask`` verify clean; single flips
+                     (test_oracle_next.py).
+* ``tensor_scale``   exact rational mean over the tensor rounded to float;
+                     one-row tensors equal ``row_scale`` (test_oracle_next.py).
 * ``dequant``        exact rational product rounded to float
                      (test_oracle_gemm.py); whole-layer cross-check against
                      a float64 re-statement of the guide's PyTorch module with
@@ -93,6 +104,10 @@ def _load():
     lib.oracle_act_quant.argtypes = [P, I64, I64, P, P]
     lib.oracle_gemm_acc.argtypes = [P, P, I64, I64, I64, P]
     lib.oracle_dequant.argtypes = [P, P, P, I64, I64, P]
+    lib.oracle_rmsnorm_act_quant.argtypes = [P, P, ctypes.c_float, I64, I64, P, P, P]
+    lib.oracle_mask_stats.argtypes = [P, P, I64, I64, I, I, P]
+    lib.oracle_tensor_scale.argtypes = [P, P, I, I64, I64]
+    lib.oracle_tensor_scale.restype = ctypes.c_float
     lib.oracle_bf16_rne.argtypes = [ctypes.c_float]
     lib.oracle_bf16_rne.restype = ctypes.c_uint16
     lib.oracle_num_threads.argtypes = []
@@ -205,6 +220,46 @@ def dequant(acc: np.ndarray, beta: np.ndarray, gamma: np.ndarray) -> np.ndarray:
     y = np.empty((T, N), dtype=np.float32)
     _load().oracle_dequant(_ptr(acc), _ptr(beta), _ptr(gamma), T, N, _ptr(y))
     return y
+
+
+def rmsnorm_act_quant(x_bf16: np.ndarray, weight: np.ndarray, eps: float,
+                      want_normed: bool = False):
+    """RMSNorm with per-channel weight, then per-token absmax int8:
+    x bf16 bits [T, K], weight fp32 [K] -> (x~ int8 [T, K], beta fp32 [T],
+    normalised fp32 [T, K] or None)."""
+    x_bf16 = _c(x_bf16, np.uint16)
+    T, K = x_bf16.shape
+    weight = _c(weight, np.float32)
+    assert weight.shape == (K,)
+    xq = np.empty((T, K), dtype=np.int8)
+    beta = np.empty(T, dtype=np.float32)
+    normed = np.empty((T, K), dtype=np.float32) if want_normed else None
+    _load().oracle_rmsnorm_act_quant(_ptr(x_bf16), _ptr(weight), ctypes.c_float(eps), T, K,
+                                     _ptr(xq), _ptr(beta), _ptr(normed))
+    return xq, beta, normed
+
+
+def mask_stats(old_bits: np.ndarray | None, new_bits: np.ndarray, rows: int, cols: int,
+               n: int, m: int) -> tuple[int, int]:
+    """(weights whose mask state changed, M-groups not keeping exactly n)."""
+    new_bits = _c(new_bits, np.uint8)
+    if old_bits is not None:
+        old_bits = _c(old_bits, np.uint8)
+    assert new_bits.size * 8 >= rows * cols and cols % m == 0
+    st = np.zeros(2, dtype=np.int64)
+    _load().oracle_mask_stats(_ptr(old_bits), _ptr(new_bits), rows, cols, n, m, _ptr(st))
+    return int(st[0]), int(st[1])
+
+
+def tensor_scale(W: np.ndarray, mask_bits: np.ndarray | None = None,
+                 from_masked: bool = False) -> np.float32:
+    """Per-tensor absmean scale (one float for the whole matrix)."""
+    W = _c(W, np.float32)
+    rows, cols = W.shape
+    if from_masked:
+        mask_bits = _c(mask_bits, np.uint8)
+    return np.float32(_load().oracle_tensor_scale(_ptr(W), _ptr(mask_bits) if from_masked else None,
+                                                  1 if from_masked else 0, rows, cols))
 
 
 def bf16_rne(f: float) -> int:

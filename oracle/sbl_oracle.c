@@ -256,6 +256,103 @@ void oracle_dequant(const int32_t* acc, const float* beta, const float* gamma,
                   (double)gamma[o] / 127.0);
 }
 
+/* ------------------------------------------------------------------------ *
+ * RMSNorm, then per-token absmax int8 quantisation of the normalised row.
+ * [guide] item 4: the activations are normalised with RMSNorm before the
+ * absmax quantisation; its module applies nn.RMSNorm(in_features) (a learned
+ * per-channel weight) to x first.  The model card's model uses norm_eps
+ * 1e-6 ([halo], "How to load"); eps is an argument here.
+ *
+ * Reading (the pages give no precision or order): with x_j the bf16 inputs
+ * widened to float (exact),
+ *   ms  = float( (sum_j x_j^2) / cols )   sum and division in double, one
+ *                                         rounding to float;
+ *   r   = 1 / sqrt(ms + eps)              each step one correctly rounded
+ *                                         float operation (add, sqrt, divide);
+ *   n_j = (x_j * r) * w_j                 two float multiplies;
+ * then beta = max(max_j |n_j|, 1e-5), s = 127/beta and
+ * x~_j = Clip(Round(n_j * s), -128, 127) exactly as oracle_act_quant does on
+ * its input.  `normed` (nullable) receives n.
+ * ------------------------------------------------------------------------ */
+void oracle_rmsnorm_act_quant(const uint16_t* x_bf16, const float* weight, float eps,
+                              int64_t tokens, int64_t cols, int8_t* xq, float* beta,
+                              float* normed) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < tokens; ++t) {
+    const uint16_t* xr = x_bf16 + t * cols;
+    double ss = 0.0;
+    for (int64_t j = 0; j < cols; ++j) {
+      double v = (double)bf16_to_float(xr[j]);
+      ss += v * v;
+    }
+    float ms = (float)(ss / (double)cols);
+    float d = ms + eps;
+    float r = 1.0f / sqrtf(d);
+    float b = 0.0f;
+    for (int64_t j = 0; j < cols; ++j) {
+      float n = (bf16_to_float(xr[j]) * r) * weight[j];
+      if (normed) normed[t * cols + j] = n;
+      float a = absf(n);
+      if (a > b) b = a;
+    }
+    if (!(b >= ORACLE_SCALE_EPS)) b = ORACLE_SCALE_EPS;
+    beta[t] = b;
+    float s = 127.0f / b;
+    for (int64_t j = 0; j < cols; ++j) {
+      float n = (bf16_to_float(xr[j]) * r) * weight[j];
+      float v = rintf(n * s);
+      if (v > 127.0f) v = 127.0f;
+      if (v < -128.0f) v = -128.0f;
+      xq[t * cols + j] = (int8_t)v;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ *
+ * Mask monitoring.  [repo] "Key Training Options": the mask change rate is
+ * monitored every few steps (--sparse_mask_monitor_interval); [halo]
+ * "Recipe": a mask-verify runs every 500 steps.  Reading: the change count
+ * is the number of weights whose kept/dropped state differs between two
+ * masks of the same matrix (the rate is that over rows*cols), and the verify
+ * count is the number of M-groups of the new mask that do not keep exactly
+ * N weights (the model card's "keep exactly N").  old_bits may be NULL
+ * (verify only; the change count is then 0).
+ * stats[0] = changed weights, stats[1] = groups not keeping exactly n.
+ * ------------------------------------------------------------------------ */
+void oracle_mask_stats(const uint8_t* old_bits, const uint8_t* new_bits, int64_t rows,
+                       int64_t cols, int n, int m, int64_t* stats) {
+  int64_t changed = 0, bad = 0;
+  const int64_t total = rows * cols;
+  for (int64_t i = 0; i < total; ++i)
+    if (old_bits && mask_bit(old_bits, i) != mask_bit(new_bits, i)) changed++;
+  for (int64_t g = 0; g < total / m; ++g) {
+    int kept = 0;
+    for (int j = 0; j < m; ++j) kept += mask_bit(new_bits, g * m + j);
+    if (kept != n) bad++;
+  }
+  stats[0] = changed;
+  stats[1] = bad;
+}
+
+/* ------------------------------------------------------------------------ *
+ * Per-tensor absmean scale.  [guide] item 2 and its module: gamma is the
+ * mean of |W| over all d_out * d_in weights, clamped below at 1e-5 (the
+ * model card's per-row scale is the default elsewhere).  Sum and division
+ * in double, one rounding to float; from_masked sums |W| * mask and still
+ * divides by rows * cols.
+ * ------------------------------------------------------------------------ */
+float oracle_tensor_scale(const float* W, const uint8_t* mask_bits, int from_masked,
+                          int64_t rows, int64_t cols) {
+  double s = 0.0;
+  for (int64_t i = 0; i < rows * cols; ++i) {
+    if (from_masked && !mask_bit(mask_bits, i)) continue;
+    s += (double)absf(W[i]);
+  }
+  float g = (float)(s / ((double)rows * (double)cols));
+  if (!(g >= ORACLE_SCALE_EPS)) g = ORACLE_SCALE_EPS;
+  return g;
+}
+
 /* Number of OpenMP threads the oracle runs with (1 when built without it). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

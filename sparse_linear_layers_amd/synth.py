@@ -50,6 +50,21 @@ def activations_bf16(tag: str, tokens: int, cols: int) -> np.ndarray:
     return float_to_bf16_bits(x)
 
 
+def norm_weight(tag: str, cols: int) -> np.ndarray:
+    """float32 [cols] per-channel RMSNorm weight ~ N(1, 0.1) (a trained
+    norm's weights sit around 1)."""
+    return (np.float32(1) + rng(tag).standard_normal(cols, dtype=np.float32)
+            * np.float32(0.1)).astype(np.float32)
+
+
+def mask_flip(tag: str, mask_bits: np.ndarray, fraction: float) -> np.ndarray:
+    """A copy of a bit-packed mask with about `fraction` of its bits
+    flipped at random (input generation for the mask-monitor tests)."""
+    bits = np.unpackbits(np.asarray(mask_bits, dtype=np.uint8), bitorder="little")
+    flip = rng(tag).random(bits.size) < fraction
+    return np.packbits(bits ^ flip.astype(np.uint8), bitorder="little")
+
+
 # ---------------------------------------------------------------------------
 # Workload shapes: (name, out_features, in_features)
 # ---------------------------------------------------------------------------
