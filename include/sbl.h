@@ -79,6 +79,11 @@ extern "C" {
 
 /* Flags of ternary_quant_pack / nm_mask_quant_pack. */
 #define SBL_SCALE_FROM_MASKED 1u /* gamma = sum(|w| * mask) / cols instead of sum(|w|) / cols */
+#define SBL_SCALE_PER_TENSOR 2u  /* one gamma for the whole matrix (guide "Mathematical
+                                    Formulation", step 2, and its module): mean |w| over
+                                    rows*cols, written into every row_scale entry; W is read
+                                    twice and `packed` holds per-row partial sums in between.
+                                    Not accepted by nm_mask_quant_pack_grouped. */
 
 /* Row-scale dtype selector of the products. */
 #define SBL_SCALE_F32 0
@@ -105,7 +110,9 @@ int nm_mask_create(const float* W, int64_t rows, int64_t cols, int n, int m,
  * Model card "Recipe" (per-row absmean) and "Packed vs raw" (layout);
  * guide "Mathematical Formulation", steps 2-3; README "Sparse-BitNet".
  *   gamma_r  = max(mean_j |W_rj|, 1e-5), the mean rounded once to float
- *              (sum of |w| * mask_rj with SBL_SCALE_FROM_MASKED);
+ *              (sum of |w| * mask_rj with SBL_SCALE_FROM_MASKED; the mean over
+ *              the whole matrix, the same in every row, with
+ *              SBL_SCALE_PER_TENSOR);
  *   code_rj  = Clip(Round(W_rj / gamma_r), -1, 1), 0 where the mask bit is
  *              0 (Round = half to even).
  *   mask_bits   uint8 [rows*cols/8] or NULL (dense BitNet: every weight
@@ -158,6 +165,44 @@ int nm_mask_quant_pack_grouped(const sbl_refresh_desc* descs_host,
  * ------------------------------------------------------------------------ */
 int act_quant_i8(const uint16_t* x_bf16, int64_t tokens, int64_t cols,
                  int8_t* xq, float* beta, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * RMSNorm, then per-token absmax int8 quantisation, in one pass over x.
+ * Guide "Mathematical Formulation", step 4 (activations are normalised with
+ * RMSNorm before the absmax quantisation) and its module in "End-to-End
+ * Implementation" (nn.RMSNorm with a per-channel weight in front of the
+ * absmax step); the model card's model uses norm_eps 1e-6.
+ *   r_t    = float(1 / sqrt(sum_j x_tj^2 / cols + eps))   (exact squares,
+ *            every step in double, one rounding to float; 0 when the
+ *            root's argument is 0)
+ *   n_tj   = (x_tj * r_t) * norm_weight_j    (two float multiplies)
+ *   then beta_t, x~_tj from n as in act_quant_i8.
+ *   x_bf16 uint16 [tokens, cols];  norm_weight float [cols];  eps >= 0
+ *   xq int8 [tokens, cols];  beta float [tokens]
+ * Errors: SBL_ERR_ARG also for a negative or non-finite eps.
+ * ------------------------------------------------------------------------ */
+int rmsnorm_act_quant_i8(const uint16_t* x_bf16, const float* norm_weight, float eps,
+                         int64_t tokens, int64_t cols, int8_t* xq, float* beta,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Mask monitoring: change count between two masks and a verify count.
+ * README "Key Training Options" (the mask change rate is monitored every
+ * few steps); model card "Recipe" (mask-verify; every group keeps exactly
+ * n).
+ *   stats[0] = number of weights whose bit differs between old_bits and
+ *              new_bits (0 when old_bits is NULL); the change rate is
+ *              stats[0] / (rows*cols)
+ *   stats[1] = number of m-groups of new_bits that do not hold exactly n
+ *              set bits
+ *   old_bits, new_bits  uint8 [rows*cols/8] (layout of nm_mask_create);
+ *                       old_bits may be NULL (and new_bits too when rows
+ *                       is 0: the counts are then zeroed)
+ *   stats               int64 [2], device memory; overwritten (zeroed by the
+ *                       call itself before counting)
+ * ------------------------------------------------------------------------ */
+int nm_mask_stats(const uint8_t* old_bits, const uint8_t* new_bits, int64_t rows,
+                  int64_t cols, int n, int m, int64_t* stats, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Packed-ternary x int8 product, prefill (dense int8 matrix cores).

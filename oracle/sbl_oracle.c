@@ -265,10 +265,11 @@ void oracle_dequant(const int32_t* acc, const float* beta, const float* gamma,
  *
  * Reading (the pages give no precision or order): with x_j the bf16 inputs
  * widened to float (exact),
- *   ms  = float( (sum_j x_j^2) / cols )   sum and division in double, one
- *                                         rounding to float;
- *   r   = 1 / sqrt(ms + eps)              each step one correctly rounded
- *                                         float operation (add, sqrt, divide);
+ *   r   = float( 1 / sqrt(sum_j x_j^2 / cols + eps) )   every step in double
+ *         (squares exact), one rounding to float at the end; r = 0 when
+ *         sum/cols + eps is 0 (an all-zero row at eps = 0 then normalises to
+ *         0 instead of 0 * inf).  Double keeps the mean of squares of any
+ *         bf16 row in range;
  *   n_j = (x_j * r) * w_j                 two float multiplies;
  * then beta = max(max_j |n_j|, 1e-5), s = 127/beta and
  * x~_j = Clip(Round(n_j * s), -128, 127) exactly as oracle_act_quant does on
@@ -285,9 +286,8 @@ void oracle_rmsnorm_act_quant(const uint16_t* x_bf16, const float* weight, float
       double v = (double)bf16_to_float(xr[j]);
       ss += v * v;
     }
-    float ms = (float)(ss / (double)cols);
-    float d = ms + eps;
-    float r = 1.0f / sqrtf(d);
+    double d = ss / (double)cols + (double)eps;
+    float r = d > 0.0 ? (float)(1.0 / sqrt(d)) : 0.0f;
     float b = 0.0f;
     for (int64_t j = 0; j < cols; ++j) {
       float n = (bf16_to_float(xr[j]) * r) * weight[j];

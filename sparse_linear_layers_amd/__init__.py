@@ -27,10 +27,12 @@ __all__ = [
     "sparse_bitlinear_gemm", "sparse24_bytes", "sparse24_compress",
     "sparse_bitlinear_gemm_sparse24", "sparse_bitlinear_gemv",
     "sparse_bitlinear_gemv_grouped", "GemvDesc", "RefreshDesc", "refresh_descs", "gemv_descs",
-    "SCALE_FROM_MASKED", "SCALE_F32", "SCALE_BF16", "GEMV_MAX_TOKENS",
+    "SCALE_FROM_MASKED", "SCALE_PER_TENSOR", "SCALE_F32", "SCALE_BF16", "GEMV_MAX_TOKENS",
+    "rmsnorm_act_quant_i8", "nm_mask_stats",
 ]
 
 SCALE_FROM_MASKED = 1
+SCALE_PER_TENSOR = 2
 SCALE_F32 = 0
 SCALE_BF16 = 1
 GEMV_MAX_TOKENS = 16
@@ -81,6 +83,8 @@ def load() -> ctypes.CDLL:
         "nm_mask_quant_pack": [P, I64, I64, I, I, U, P, P, P, P, P],
         "nm_mask_quant_pack_grouped": [P, P, I, I, I, U, P],
         "act_quant_i8": [P, I64, I64, P, P, P],
+        "rmsnorm_act_quant_i8": [P, P, ctypes.c_float, I64, I64, P, P, P],
+        "nm_mask_stats": [P, P, I64, I64, I, I, P, P],
         "sparse_bitlinear_gemm": [P, P, P, P, I, I64, I64, I64, P, P, P],
         "sparse24_compress": [P, I64, I64, P, P, P],
         "sparse_bitlinear_gemm_sparse24": [P, P, P, P, I, I64, I64, I64, P, P, P],
@@ -144,6 +148,7 @@ def nm_mask_create(W: torch.Tensor, n: int, m: int, out: torch.Tensor | None = N
     rows, cols = W.shape
     if out is None:
         out = torch.empty(rows * cols // 8, dtype=torch.uint8, device=W.device)
+    _shape(out, (rows * cols // 8,), torch.uint8, "out")
     _check("nm_mask_create", load().nm_mask_create(_ptr(W), rows, cols, n, m, _ptr(out),
                                                    _stream(W.device)))
     return out
@@ -153,9 +158,9 @@ def ternary_quant_pack(W: torch.Tensor, mask_bits: torch.Tensor | None = None,
                        flags: int = 0, want_bf16: bool = True):
     """-> (packed uint8 [rows, cols/4], scale float32 [rows], scale_bf16 int16 bits or None)."""
     _need(W, torch.float32, "W", 2)
-    if mask_bits is not None:
-        _need(mask_bits, torch.uint8, "mask_bits")
     rows, cols = W.shape
+    if mask_bits is not None:
+        _shape(mask_bits, (rows * cols // 8,), torch.uint8, "mask_bits")
     dev = W.device
     packed = torch.empty((rows, cols // 4), dtype=torch.uint8, device=dev)
     scale = torch.empty(rows, dtype=torch.float32, device=dev)
@@ -229,6 +234,43 @@ def nm_mask_quant_pack_grouped(host, devbuf, count: int, n: int, m: int, flags: 
     passes the launch."""
     _check("nm_mask_quant_pack_grouped", load().nm_mask_quant_pack_grouped(
         ctypes.cast(host, ctypes.c_void_p), _ptr(devbuf), count, n, m, flags, _stream(device)))
+
+
+def rmsnorm_act_quant_i8(x: torch.Tensor, norm_weight: torch.Tensor, eps: float = 1e-6,
+                         xq: torch.Tensor | None = None, beta: torch.Tensor | None = None):
+    """RMSNorm (per-channel float32 weight [cols], eps) then per-token absmax
+    int8: x bfloat16 [tokens, cols] -> (xq int8 [tokens, cols], beta float32
+    [tokens])."""
+    _need(x, _BF16_BITS, "x", 2)
+    T, K = x.shape
+    _shape(norm_weight, (K,), torch.float32, "norm_weight")
+    if xq is None:
+        xq = torch.empty((T, K), dtype=torch.int8, device=x.device)
+    if beta is None:
+        beta = torch.empty(T, dtype=torch.float32, device=x.device)
+    _shape(xq, (T, K), torch.int8, "xq")
+    _shape(beta, (T,), torch.float32, "beta")
+    _check("rmsnorm_act_quant_i8", load().rmsnorm_act_quant_i8(
+        _ptr(x), _ptr(norm_weight), ctypes.c_float(eps), T, K, _ptr(xq), _ptr(beta),
+        _stream(x.device)))
+    return xq, beta
+
+
+def nm_mask_stats(old_bits: torch.Tensor | None, new_bits: torch.Tensor, rows: int, cols: int,
+                  n: int, m: int, stats: torch.Tensor | None = None) -> torch.Tensor:
+    """Mask monitor counts as an int64 device tensor [2]: weights whose mask
+    bit changed from old_bits (0 without it) and m-groups of new_bits not
+    keeping exactly n."""
+    nbytes = rows * cols // 8
+    _shape(new_bits, (nbytes,), torch.uint8, "new_bits")
+    if old_bits is not None:
+        _shape(old_bits, (nbytes,), torch.uint8, "old_bits")
+    if stats is None:
+        stats = torch.empty(2, dtype=torch.int64, device=new_bits.device)
+    _shape(stats, (2,), torch.int64, "stats")
+    _check("nm_mask_stats", load().nm_mask_stats(
+        _ptr(old_bits), _ptr(new_bits), rows, cols, n, m, _ptr(stats), _stream(new_bits.device)))
+    return stats
 
 
 def act_quant_i8(x: torch.Tensor, xq: torch.Tensor | None = None,

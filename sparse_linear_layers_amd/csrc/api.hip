@@ -61,7 +61,7 @@ int ternary_quant_pack(const float* W, const uint8_t* mask_bits, int64_t rows, i
                        hipStream_t stream) {
   if (rows < 0 || rows > kMaxRows) return SBL_ERR_ARG;
   if (int s = check_cols(cols)) return s;
-  if (flags & ~SBL_SCALE_FROM_MASKED) return SBL_ERR_UNSUPPORTED;
+  if (flags & ~(SBL_SCALE_FROM_MASKED | SBL_SCALE_PER_TENSOR)) return SBL_ERR_UNSUPPORTED;
   if (rows == 0) return SBL_OK;
   if (!W || !packed || !row_scale) return SBL_ERR_ARG;
   if ((flags & SBL_SCALE_FROM_MASKED) && !mask_bits) return SBL_ERR_ARG;
@@ -79,7 +79,7 @@ int nm_mask_quant_pack(const float* W, int64_t rows, int64_t cols, int n, int m,
   if (rows < 0 || rows > kMaxRows) return SBL_ERR_ARG;
   if (int s = check_cols(cols)) return s;
   if (int s = check_nm(n, m)) return s;
-  if (flags & ~SBL_SCALE_FROM_MASKED) return SBL_ERR_UNSUPPORTED;
+  if (flags & ~(SBL_SCALE_FROM_MASKED | SBL_SCALE_PER_TENSOR)) return SBL_ERR_UNSUPPORTED;
   if (rows == 0) return SBL_OK;
   if (!W || !packed || !row_scale) return SBL_ERR_ARG;
   if (!aligned16(W) || !aligned16_or_null(mask_bits) || !aligned16(packed) ||
@@ -113,6 +113,33 @@ int nm_mask_quant_pack_grouped(const sbl_refresh_desc* descs_host,
   if (total_blocks > INT32_MAX / 2) return SBL_ERR_ARG;
   (void)hipGetLastError();
   return hip_status(sbl::launch_quant_pack_grouped(descs_host, descs_dev, count, n, m, flags, stream));
+}
+
+int rmsnorm_act_quant_i8(const uint16_t* x_bf16, const float* norm_weight, float eps,
+                         int64_t tokens, int64_t cols, int8_t* xq, float* beta,
+                         hipStream_t stream) {
+  if (tokens < 0 || tokens > kMaxRows) return SBL_ERR_ARG;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return SBL_ERR_ARG;  // rejects NaN and inf
+  if (int s = check_cols(cols)) return s;
+  if (tokens == 0) return SBL_OK;
+  if (!x_bf16 || !norm_weight || !xq || !beta) return SBL_ERR_ARG;
+  if (!aligned16(x_bf16) || !aligned16(norm_weight) || !aligned16(xq) || !aligned16(beta))
+    return SBL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(sbl::launch_rmsnorm_act_quant(x_bf16, norm_weight, eps, tokens, cols, xq, beta,
+                                                  stream));
+}
+
+int nm_mask_stats(const uint8_t* old_bits, const uint8_t* new_bits, int64_t rows, int64_t cols,
+                  int n, int m, int64_t* stats, hipStream_t stream) {
+  if (rows < 0 || rows > kMaxRows) return SBL_ERR_ARG;
+  if (int s = check_cols(cols)) return s;
+  if (int s = check_nm(n, m)) return s;
+  if (!stats || (rows > 0 && !new_bits)) return SBL_ERR_ARG;
+  if (!aligned16_or_null(old_bits) || !aligned16(new_bits) || (reinterpret_cast<uintptr_t>(stats) & 7u))
+    return SBL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(sbl::launch_mask_stats(old_bits, new_bits, rows, cols, n, m, stats, stream));
 }
 
 int act_quant_i8(const uint16_t* x_bf16, int64_t tokens, int64_t cols, int8_t* xq, float* beta,

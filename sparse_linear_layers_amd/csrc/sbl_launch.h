@@ -25,6 +25,10 @@ hipError_t launch_quant_pack(const float* W, const uint8_t* mask_in, int64_t row
                              hipStream_t stream);
 hipError_t launch_quant_pack_grouped(const sbl_refresh_desc* host, const sbl_refresh_desc* dev,
                                      int count, int n, int m, unsigned flags, hipStream_t stream);
+hipError_t launch_mask_stats(const uint8_t* old_bits, const uint8_t* new_bits, int64_t rows,
+                             int64_t cols, int n, int m, int64_t* stats, hipStream_t stream);
+hipError_t launch_rmsnorm_act_quant(const uint16_t* x, const float* w, float eps, int64_t tokens,
+                                    int64_t cols, int8_t* xq, float* beta, hipStream_t stream);
 hipError_t launch_act_quant(const uint16_t* x, int64_t tokens, int64_t cols, int8_t* xq,
                             float* beta, hipStream_t stream);
 hipError_t launch_gemm(const int8_t* xq, const float* beta, const uint8_t* packed,

@@ -67,6 +67,7 @@ struct RowJob {
   uint16_t* scale_bf16;
   int64_t rows;
   int64_t cols;
+  const float* scale_in;  // non-null: the row's scale is given (per-tensor gamma)
 };
 
 template <int CPL, int MODE>
@@ -114,17 +115,21 @@ __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, i
     }
   }
   // ---- scale: sum of |w| in double, lane partials then a butterfly ----
-  double s = 0.0;
+  float g;
+  if (job.scale_in) {
+    g = job.scale_in[row];
+  } else {
+    double s = 0.0;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const float a[4] = {fabsf(v[c].x), fabsf(v[c].y), fabsf(v[c].z), fabsf(v[c].w)};
+    for (int c = 0; c < CPL; ++c) {
+      const float a[4] = {fabsf(v[c].x), fabsf(v[c].y), fabsf(v[c].z), fabsf(v[c].w)};
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (!from_masked || ((keep[c] >> e) & 1u)) s += (double)a[e];
+      for (int e = 0; e < 4; ++e)
+        if (!from_masked || ((keep[c] >> e) & 1u)) s += (double)a[e];
+    }
+    s = wave_sum(s);
+    g = fmaxf((float)(s / (double)cols), 1e-5f);
   }
-  s = wave_sum(s);
-  float g = (float)(s / (double)cols);
-  g = fmaxf(g, 1e-5f);
   // Clip(Round(w/g), -1, 1) is +-1 exactly when |w| > g/2 (g/2 is exact for
   // g >= 1e-5, and w/g rounded to float exceeds 1/2 iff |w| > g/2).
   const float thr = g * 0.5f;
@@ -192,17 +197,22 @@ __device__ void quant_pack_row_long(const RowJob& job, int64_t row, int n, bool 
       return low_half ? (k8 & 0xFu) : (k8 >> 4);
     }
   };
-  double s = 0.0;
-  for (int64_t base = 0; base < nchunks; base += kWave) {  // nchunks % 16 == 0
-    const int64_t idx = base + lane;
-    float4 x = idx < nchunks ? src[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
-    uint32_t k = mask_of(idx, x);
-    const float a[4] = {fabsf(x.x), fabsf(x.y), fabsf(x.z), fabsf(x.w)};
-    for (int e = 0; e < 4; ++e)
-      if (!from_masked || ((k >> e) & 1u)) s += (double)a[e];
+  float g;
+  if (job.scale_in) {
+    g = job.scale_in[row];
+  } else {
+    double s = 0.0;
+    for (int64_t base = 0; base < nchunks; base += kWave) {  // nchunks % 16 == 0
+      const int64_t idx = base + lane;
+      float4 x = idx < nchunks ? src[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+      uint32_t k = mask_of(idx, x);
+      const float a[4] = {fabsf(x.x), fabsf(x.y), fabsf(x.z), fabsf(x.w)};
+      for (int e = 0; e < 4; ++e)
+        if (!from_masked || ((k >> e) & 1u)) s += (double)a[e];
+    }
+    s = wave_sum(s);
+    g = fmaxf((float)(s / (double)cols), 1e-5f);
   }
-  s = wave_sum(s);
-  float g = fmaxf((float)(s / (double)cols), 1e-5f);
   const float thr = g * 0.5f;
   uint32_t* dst = reinterpret_cast<uint32_t*>(job.packed + row * (cols >> 2));
   for (int64_t base = 0; base < nchunks; base += kWave) {
@@ -281,6 +291,150 @@ __global__ __launch_bounds__(256) void quant_pack_grouped_kernel(GroupedRefreshA
 }
 
 // ---------------------------------------------------------------------------
+// Per-tensor absmean ("Sparse-BitNet Guide", "Mathematical Formulation",
+// step 2, and its module: one gamma = mean |W| over the whole matrix).
+// Three launches, because no code can be decided before the whole tensor
+// is summed: (1) one wave per row sums |w| (or |w| * mask) in double and
+// parks the sum in the first 8 bytes of the row's packed output, which the
+// codes overwrite later; (2) one block adds the row sums in a fixed order
+// and writes gamma into every row scale; (3) the row kernel quantises with
+// the given scale.  W is read twice (8.25 B per weight instead of 4.25).
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(256) void row_abs_sum_kernel(RowJob job, int n, int from_masked) {
+  const int lane = lane_id();
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= job.rows) return;
+  const int64_t cols = job.cols;
+  const int64_t nchunks = cols >> 2;
+  const float4* src = reinterpret_cast<const float4*>(job.W + row * cols);
+  double s = 0.0;
+  for (int64_t base = 0; base < nchunks; base += kWave) {  // nchunks % 16 == 0
+    const int64_t idx = base + lane;
+    const float4 x = idx < nchunks ? src[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t k = 0xFu;
+    if (from_masked) {
+      if constexpr (MODE == 0) {
+        const int64_t bit = row * cols + 4 * idx;
+        k = idx < nchunks ? (job.mask_in[bit >> 3] >> (bit & 7)) & 0xFu : 0u;
+      } else if constexpr (MODE == 1) {
+        uint32_t key[4] = {abs_key(x.x), abs_key(x.y), abs_key(x.z), abs_key(x.w)};
+        k = keep_mask<4>(key, n);
+      } else {
+        uint32_t mine[4] = {abs_key(x.x), abs_key(x.y), abs_key(x.z), abs_key(x.w)};
+        uint32_t other[4];
+        for (int e = 0; e < 4; ++e) other[e] = (uint32_t)shfl_xor((int)mine[e], 1);
+        const bool low_half = (lane & 1) == 0;
+        uint32_t key[8];
+        for (int e = 0; e < 4; ++e) {
+          key[e] = low_half ? mine[e] : other[e];
+          key[4 + e] = low_half ? other[e] : mine[e];
+        }
+        const uint32_t k8 = keep_mask<8>(key, n);
+        k = low_half ? (k8 & 0xFu) : (k8 >> 4);
+      }
+    }
+    const float a[4] = {fabsf(x.x), fabsf(x.y), fabsf(x.z), fabsf(x.w)};
+    for (int e = 0; e < 4; ++e)
+      if ((k >> e) & 1u) s += (double)a[e];
+  }
+  s = wave_sum(s);
+  if (lane == 0) *reinterpret_cast<double*>(job.packed + row * (cols >> 2)) = s;
+}
+
+__global__ __launch_bounds__(256) void tensor_scale_kernel(RowJob job) {
+  __shared__ double part[256];
+  const int t = threadIdx.x;
+  const int64_t stride = job.cols >> 2;
+  double s = 0.0;
+  for (int64_t r = t; r < job.rows; r += 256)
+    s += *reinterpret_cast<const double*>(job.packed + r * stride);
+  part[t] = s;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {  // fixed pairing order: deterministic
+    if (t < h) part[t] += part[t + h];
+    __syncthreads();
+  }
+  const float g = fmaxf((float)(part[0] / ((double)job.rows * (double)job.cols)), 1e-5f);
+  for (int64_t r = t; r < job.rows; r += 256) {
+    job.scale[r] = g;
+    if (job.scale_bf16) job.scale_bf16[r] = f32_to_bf16_rne(g);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Mask monitoring (README "Key Training Options": the mask change rate is
+// monitored every few steps; model card "Recipe": a mask-verify every 500
+// steps).  stats[0] += weights whose mask bit differs between two masks,
+// stats[1] += M-groups of the new mask that do not keep exactly n.  The
+// masks are flat bit streams (groups never straddle rows, cols % 64 == 0),
+// read 16 bytes per lane; group counts come from in-register popcounts.
+// ---------------------------------------------------------------------------
+__global__ void zero_stats_kernel(unsigned long long* stats) {
+  if (threadIdx.x < 2) stats[threadIdx.x] = 0ull;
+}
+
+template <int M>
+__device__ __forceinline__ uint32_t groups_not_n(uint32_t w, uint32_t n) {
+  uint32_t v = w - ((w >> 1) & 0x55555555u);           // 2-bit counts
+  v = (v & 0x33333333u) + ((v >> 2) & 0x33333333u);    // 4-bit counts (groups of 4)
+  uint32_t x;
+  if constexpr (M == 4) {
+    x = v ^ (n * 0x11111111u);
+    x = (x | (x >> 1) | (x >> 2) | (x >> 3)) & 0x11111111u;
+  } else {
+    v = (v + (v >> 4)) & 0x0F0F0F0Fu;                   // 8-bit counts (groups of 8)
+    x = v ^ (n * 0x01010101u);
+    x = (x | (x >> 1) | (x >> 2) | (x >> 3)) & 0x01010101u;
+  }
+  return (uint32_t)__popc(x);
+}
+
+template <int M>
+__global__ __launch_bounds__(256) void mask_stats_kernel(const uint32_t* __restrict__ old_w,
+                                                         const uint32_t* __restrict__ new_w,
+                                                         int64_t words, int n,
+                                                         unsigned long long* stats) {
+  __shared__ uint32_t part[2][4];
+  uint32_t changed = 0, bad = 0;
+  const int64_t nvec = words >> 2;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t gsz = (int64_t)gridDim.x * blockDim.x;
+  auto word = [&](uint32_t a, uint32_t b) {
+    changed += (uint32_t)__popc(a ^ b);
+    bad += groups_not_n<M>(a, (uint32_t)n);
+  };
+  for (int64_t i = gid; i < nvec; i += gsz) {
+    const uint4 a = reinterpret_cast<const uint4*>(new_w)[i];
+    const uint4 b = old_w ? reinterpret_cast<const uint4*>(old_w)[i] : a;
+    word(a.x, b.x);
+    word(a.y, b.y);
+    word(a.z, b.z);
+    word(a.w, b.w);
+  }
+  for (int64_t i = 4 * nvec + gid; i < words; i += gsz) word(new_w[i], old_w ? old_w[i] : new_w[i]);
+  // per-block sums (each under 2^32 for any launch this library makes),
+  // then one 64-bit atomic per counter
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    changed += (uint32_t)shfl_xor((int)changed, d);
+    bad += (uint32_t)shfl_xor((int)bad, d);
+  }
+  const int wave = threadIdx.x >> 6;
+  if (lane_id() == 0) {
+    part[0][wave] = changed;
+    part[1][wave] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t c = part[0][0] + part[0][1] + part[0][2] + part[0][3];
+    const uint32_t g = part[1][0] + part[1][1] + part[1][2] + part[1][3];
+    if (c) atomicAdd(&stats[0], (unsigned long long)c);
+    if (g) atomicAdd(&stats[1], (unsigned long long)g);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
 // Register footprint class of a row: 4-column chunks each lane holds.
@@ -324,10 +478,20 @@ hipError_t launch_quant_pack(const float* W, const uint8_t* mask_in, int64_t row
                              int n, int m, int fuse_mask, unsigned flags, uint8_t* mask_out,
                              uint8_t* packed, float* scale, uint16_t* scale_bf16,
                              hipStream_t stream) {
-  RowJob job{W, mask_in, mask_out, packed, scale, scale_bf16, rows, cols};
+  RowJob job{W, mask_in, mask_out, packed, scale, scale_bf16, rows, cols, nullptr};
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   const int cpl = chunks_per_lane(cols);
   const int fm = (flags & SBL_SCALE_FROM_MASKED) ? 1 : 0;
+  if (flags & SBL_SCALE_PER_TENSOR) {
+    if (!fuse_mask)
+      hipLaunchKernelGGL(row_abs_sum_kernel<0>, grid, dim3(256), 0, stream, job, n, fm);
+    else if (m == 4)
+      hipLaunchKernelGGL(row_abs_sum_kernel<1>, grid, dim3(256), 0, stream, job, n, fm);
+    else
+      hipLaunchKernelGGL(row_abs_sum_kernel<2>, grid, dim3(256), 0, stream, job, n, fm);
+    hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(256), 0, stream, job);
+    job.scale_in = scale;
+  }
   if (!fuse_mask)
     launch_row<0>(cpl, grid, stream, job, n, fm);
   else if (m == 4)
@@ -350,6 +514,21 @@ static void launch_grouped(int cpl, dim3 grid, hipStream_t stream, const Grouped
     SBL_CASE(24) SBL_CASE(28) SBL_CASE(32) SBL_CASE(0)
 #undef SBL_CASE
   }
+}
+
+hipError_t launch_mask_stats(const uint8_t* old_bits, const uint8_t* new_bits, int64_t rows,
+                             int64_t cols, int n, int m, int64_t* stats, hipStream_t stream) {
+  unsigned long long* st = reinterpret_cast<unsigned long long*>(stats);
+  hipLaunchKernelGGL(zero_stats_kernel, dim3(1), dim3(64), 0, stream, st);
+  const int64_t words = rows * cols / 32;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((words / 4 + 255) / 256, 2048));
+  const uint32_t* ow = reinterpret_cast<const uint32_t*>(old_bits);
+  const uint32_t* nw = reinterpret_cast<const uint32_t*>(new_bits);
+  if (m == 4)
+    hipLaunchKernelGGL(mask_stats_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, ow, nw, words, n, st);
+  else
+    hipLaunchKernelGGL(mask_stats_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, ow, nw, words, n, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_pack_grouped(const sbl_refresh_desc* host, const sbl_refresh_desc* dev,

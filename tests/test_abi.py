@@ -64,7 +64,7 @@ def test_quant_validation(lib):
     f = lib.ternary_quant_pack
     assert f(P, None, 4, 64, 0, None, P, None, None) == ARG
     assert f(P, None, 4, 64, 1, P, P, None, None) == ARG       # from-masked needs a mask
-    assert f(P, None, 4, 64, 2, P, P, None, None) == UNSUP     # unknown flag
+    assert f(P, None, 4, 64, 4, P, P, None, None) == UNSUP     # unknown flag
     assert f(P, None, 4, 96, 0, P, P, None, None) == SHAPE
     assert f(P, None, 4, 64, 0, P, P, MIS, None) == ALIGN
     assert f(P, None, 0, 64, 0, P, P, None, None) == OK
@@ -115,3 +115,44 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "liboracle" not in text, fn
                 assert "sbl_oracle" not in text, fn
+
+
+def test_rmsnorm_act_quant_validation(lib):
+    f = lib.rmsnorm_act_quant_i8
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(P, P, 1e-6, 0, 64, P, P, None) == OK          # empty: nothing launched
+    assert f(P, P, -1.0, 4, 64, P, P, None) == ARG         # negative eps
+    assert f(P, P, float("nan"), 4, 64, P, P, None) == ARG
+    assert f(P, P, float("inf"), 4, 64, P, P, None) == ARG
+    assert f(P, None, 1e-6, 4, 64, P, P, None) == ARG      # the norm weight is required
+    assert f(P, P, 1e-6, 4, 96, P, P, None) == SHAPE
+    assert f(P, MIS, 1e-6, 4, 64, P, P, None) == ALIGN
+    assert f(P, P, 1e-6, -2, 64, P, P, None) == ARG
+
+
+def test_mask_stats_validation(lib):
+    f = lib.nm_mask_stats
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(P, None, 4, 64, 3, 4, P, None) == ARG         # new mask required
+    assert f(P, P, 4, 64, 3, 4, None, None) == ARG         # counters required
+    assert f(P, P, 4, 96, 3, 4, P, None) == SHAPE
+    assert f(P, P, 4, 64, 3, 6, P, None) == UNSUP
+    assert f(P, P, 4, 64, 5, 4, P, None) == UNSUP
+    assert f(MIS, P, 4, 64, 3, 4, P, None) == ALIGN
+    assert f(P, P, 4, 64, 3, 4, P + 4, None) == ALIGN     # int64 counters: 8-byte aligned
+
+
+def test_per_tensor_flag(lib):
+    tq = lib.ternary_quant_pack
+    assert tq(P, None, 0, 64, 2, P, P, None, None) == OK   # SBL_SCALE_PER_TENSOR accepted
+    assert tq(P, None, 0, 64, 3, P, P, None, None) == OK   # with SBL_SCALE_FROM_MASKED
+    assert tq(P, None, 4, 64, 3, P, P, None, None) == ARG  # from-masked needs a mask
+    assert tq(P, None, 0, 64, 4, P, P, None, None) == UNSUP
+    mq = lib.nm_mask_quant_pack
+    assert mq(P, 0, 64, 3, 4, 2, None, P, P, None, None) == OK
+    assert mq(P, 0, 64, 3, 4, 8, None, P, P, None, None) == UNSUP
+    # the grouped refresh keeps per-row scales only
+    g = lib.nm_mask_quant_pack_grouped
+    assert g(P, P, 1, 3, 4, 2, None) == UNSUP

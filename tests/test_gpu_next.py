@@ -1,0 +1,165 @@
+"""GPU parity of the operators around the forward path: RMSNorm fused into
+the int8 activation quantisation, mask change/verify counts, and the
+per-tensor absmean scale.  Through the C ABI, against the CPU oracle on the
+same seeded inputs; bit-exact everywhere (codes, scales, x~, beta, counts).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from brute import unpack_bits
+
+from sparse_linear_layers_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def sbl():
+    import sparse_linear_layers_amd as m
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.load()
+    return m
+
+
+def dev(a):
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------ RMSNorm -> int8
+@pytest.mark.parametrize("T,K", [(1, 64), (3, 256), (128, 896), (77, 4864), (5, 8192),
+                                 (4, 9216), (2, 65536)])
+@pytest.mark.parametrize("eps", [1e-6, 0.0, 1.1920928955078125e-07])
+def test_rmsnorm_act_quant(sbl, T, K, eps):
+    x = synth.activations_bf16(f"gpu/rms/{T}x{K}", T, K)
+    w = synth.norm_weight(f"gpu/rms/{K}/w", K)
+    xq_ref, beta_ref, _ = oracle.rmsnorm_act_quant(x, w, eps)
+    xq, beta = sbl.rmsnorm_act_quant_i8(dev(x), dev(w), eps)
+    assert np.array_equal(host(beta), beta_ref)
+    assert np.array_equal(host(xq), xq_ref)
+
+
+def test_rmsnorm_act_quant_edge_tokens(sbl):
+    K = 896
+    x = synth.activations_bf16("gpu/rms/edge", 6, K)
+    x[0] = 0                                                    # zero token
+    x[1] = synth.float_to_bf16_bits(np.full(K, -2.5, np.float32))  # constant token
+    x[2] = synth.float_to_bf16_bits(synth.rng("gpu/rms/edge/big").standard_normal(K).astype(np.float32) * np.float32(1e30))
+    x[3] = synth.float_to_bf16_bits(synth.rng("gpu/rms/edge/small").standard_normal(K).astype(np.float32) * np.float32(1e-18))
+    x[4, :] = 0
+    x[4, 17] = synth.float_to_bf16_bits(np.array([3.0], np.float32))[0]  # one spike
+    w = synth.norm_weight("gpu/rms/edge/w", K)
+    w[5] = 0.0
+    for eps in (1e-6, 0.0):
+        xq_ref, beta_ref, _ = oracle.rmsnorm_act_quant(x, w, eps)
+        xq, beta = sbl.rmsnorm_act_quant_i8(dev(x), dev(w), eps)
+        assert np.array_equal(host(beta), beta_ref)
+        assert np.array_equal(host(xq), xq_ref)
+
+
+@pytest.mark.parametrize("K", [896, 4864])
+def test_rmsnorm_act_quant_full_size(sbl, K):
+    """The 0.5B skeleton's prefill activations (32768 tokens), compared in
+    full."""
+    T = synth.QWEN05B_PREFILL_TOKENS
+    x = synth.activations_bf16(f"gpu/rms/full/{K}", T, K)
+    w = synth.norm_weight(f"gpu/rms/full/{K}/w", K)
+    xq_ref, beta_ref, _ = oracle.rmsnorm_act_quant(x, w, 1e-6)
+    xq, beta = sbl.rmsnorm_act_quant_i8(dev(x), dev(w), 1e-6)
+    assert np.array_equal(host(beta), beta_ref)
+    assert np.array_equal(host(xq), xq_ref)
+
+
+# --------------------------------------------------------- mask monitor
+@pytest.mark.parametrize("rows,cols,n,m", [(3, 64, 3, 4), (37, 256, 2, 4), (512, 896, 3, 4),
+                                           (64, 4864, 6, 8), (9, 1024, 4, 8), (1, 65536, 1, 4)])
+@pytest.mark.parametrize("frac", [0.0, 0.003, 0.5])
+def test_mask_stats(sbl, rows, cols, n, m, frac):
+    W = synth.latent_weight(f"gpu/ms/{rows}x{cols}", rows, cols)
+    new = host(sbl.nm_mask_create(dev(W), n, m))
+    assert np.array_equal(new, oracle.nm_mask(W, n, m))
+    old = synth.mask_flip(f"gpu/ms/{rows}x{cols}/{frac}", new, frac)
+    bad = synth.mask_flip(f"gpu/ms/{rows}x{cols}/{frac}/bad", new, frac / 3)
+    for o, nw in ((old, new), (new, old), (None, new), (None, bad), (old, bad)):
+        got = host(sbl.nm_mask_stats(None if o is None else dev(o), dev(nw), rows, cols, n, m))
+        assert tuple(int(v) for v in got) == oracle.mask_stats(o, nw, rows, cols, n, m)
+
+
+def test_mask_stats_full_layer(sbl):
+    """Every mask of one 0.5B-skeleton layer refreshed against a perturbed
+    copy of the latent weights: the change counts of the seven matrices."""
+    for name, N, K in synth.QWEN05B_LINEARS:
+        W = synth.latent_weight(f"gpu/ms/layer/{name}", N, K)
+        W2 = W + synth.latent_weight(f"gpu/ms/layer/{name}/step", N, K, std=1e-4)
+        a = sbl.nm_mask_create(dev(W), 3, 4)
+        b = sbl.nm_mask_create(dev(W2), 3, 4)
+        got = host(sbl.nm_mask_stats(a, b, N, K, 3, 4))
+        ref = oracle.mask_stats(oracle.nm_mask(W, 3, 4), oracle.nm_mask(W2, 3, 4), N, K, 3, 4)
+        assert tuple(int(v) for v in got) == ref and ref[1] == 0 and ref[0] > 0
+
+
+def test_mask_stats_empty(sbl):
+    st = sbl.nm_mask_stats(None, torch.zeros(0, dtype=torch.uint8, device=DEV), 0, 64, 3, 4)
+    assert host(st).tolist() == [0, 0]
+
+
+# ----------------------------------------------------- per-tensor gamma
+def _per_tensor_ref(W, mask, from_masked):
+    g = oracle.tensor_scale(W, mask, from_masked)
+    rows = W.shape[0]
+    gam = np.full(rows, g, dtype=np.float32)
+    codes = oracle.ternary_codes(W, mask, gam)
+    return g, oracle.pack_codes(codes)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 64), (37, 896), (512, 4864), (2048, 2048), (7, 9216)])
+@pytest.mark.parametrize("mode", ["dense", "mask", "mask_from_masked"])
+def test_ternary_quant_pack_per_tensor(sbl, rows, cols, mode):
+    W = synth.latent_weight(f"gpu/pt/{rows}x{cols}", rows, cols)
+    mask = oracle.nm_mask(W, 3, 4) if mode != "dense" else None
+    fm = mode == "mask_from_masked"
+    g, packed_ref = _per_tensor_ref(W, mask, fm)
+    flags = sbl.SCALE_PER_TENSOR | (sbl.SCALE_FROM_MASKED if fm else 0)
+    packed, scale, sb = sbl.ternary_quant_pack(dev(W), dev(mask) if mask is not None else None, flags)
+    assert (host(scale) == g).all()
+    assert (host(sb).view(np.uint16) == oracle.bf16_rne(float(g))).all()
+    assert np.array_equal(host(packed), packed_ref)
+
+
+@pytest.mark.parametrize("n,m", [(3, 4), (2, 4), (6, 8)])
+@pytest.mark.parametrize("rows,cols", [(21, 896), (16, 4864), (4, 9216)])
+@pytest.mark.parametrize("fm", [False, True])
+def test_nm_mask_quant_pack_per_tensor(sbl, n, m, rows, cols, fm):
+    W = synth.latent_weight(f"gpu/ptf/{rows}x{cols}/{n}{m}", rows, cols)
+    mask_ref = oracle.nm_mask(W, n, m)
+    g, packed_ref = _per_tensor_ref(W, mask_ref, fm)
+    flags = sbl.SCALE_PER_TENSOR | (sbl.SCALE_FROM_MASKED if fm else 0)
+    mask, packed, scale, sb = sbl.nm_mask_quant_pack(dev(W), n, m, flags)
+    assert np.array_equal(host(mask), mask_ref)
+    assert (host(scale) == g).all()
+    assert np.array_equal(host(packed), packed_ref)
+
+
+def test_per_tensor_full_size_matrix(sbl):
+    """The 0.5B skeleton's gate matrix (4864 x 896) with one scale."""
+    W = synth.latent_weight("gpu/pt/gate", 4864, 896)
+    g, packed_ref = _per_tensor_ref(W, oracle.nm_mask(W, 3, 4), False)
+    _, packed, scale, _ = sbl.nm_mask_quant_pack(dev(W), 3, 4, sbl.SCALE_PER_TENSOR)
+    assert (host(scale) == g).all()
+    assert np.array_equal(host(packed), packed_ref)
+    # the products take the replicated scale unchanged
+    x = synth.activations_bf16("gpu/pt/gate/x", 96, 896)
+    xq, beta = oracle.act_quant(x)
+    y, acc = sbl.sparse_bitlinear_gemm(dev(xq), dev(beta), packed, scale, want_acc=True)
+    codes = oracle.unpack_codes(packed_ref, 896)
+    assert np.array_equal(host(acc), oracle.gemm_acc(xq, codes))

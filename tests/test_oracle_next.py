@@ -18,22 +18,20 @@ def _bf16_to_f32(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def _exact_sqrt_to_f32(q: Fraction) -> float:
-    """Correctly rounded float32 square root of an exact rational: a
-    60-digit decimal root is far inside the rounding interval unless the
-    root sits on a midpoint, which the assertion below would expose."""
-    root = Decimal(q.numerator) / Decimal(q.denominator)
-    root = root.sqrt()
-    return exact_to_f32(Fraction(root))
+def _exact_inv_root_to_f32(q: Fraction) -> float:
+    """float32 nearest to 1/sqrt(q), from a 60-digit decimal evaluation."""
+    v = Decimal(q.numerator) / Decimal(q.denominator)
+    return exact_to_f32(Fraction(Decimal(1) / v.sqrt()))
 
 
 def _rms_steps(xrow: np.ndarray, w: np.ndarray, eps: float):
-    """Each float step of the reading, re-derived exactly."""
+    """The reading's value of r and each float step after it, from exact
+    arithmetic: r is the float nearest to the exact 1/sqrt(mean(x^2) + eps)
+    (the double evaluation rounds the same way unless the exact value sits
+    within a double ulp of a float midpoint, which these rows do not)."""
     xs = [Fraction(float(v)) for v in xrow]
-    ms = exact_to_f32(sum(v * v for v in xs) / len(xs))
-    d = exact_to_f32(Fraction(ms) + Fraction(float(np.float32(eps))))
-    sq = _exact_sqrt_to_f32(Fraction(d))
-    r = exact_to_f32(Fraction(1) / Fraction(sq))
+    q = sum(v * v for v in xs) / len(xs) + Fraction(float(np.float32(eps)))
+    r = _exact_inv_root_to_f32(q) if q > 0 else 0.0
     n = [exact_to_f32(Fraction(exact_to_f32(v * Fraction(r))) * Fraction(float(wj)))
          for v, wj in zip(xs, w)]
     return r, n
@@ -120,12 +118,29 @@ def test_rmsnorm_zero_and_constant_rows():
     x[1] = synth.float_to_bf16_bits(np.full(K, 0.75, np.float32))
     x[2] = synth.float_to_bf16_bits(np.full(K, -3.0, np.float32))
     w = np.ones(K, dtype=np.float32)
-    xq, beta, normed = oracle.rmsnorm_act_quant(x, w, 1e-6, want_normed=True)
-    # zero row: n = 0, beta clamps, codes vanish
-    assert (normed[0] == 0).all() and beta[0] == np.float32(1e-5) and (xq[0] == 0).all()
-    # constant rows normalise to +-1 up to eps: every code is +-127
-    assert np.abs(np.abs(normed[1:]) - 1).max() < 1e-5
-    assert (xq[1] == 127).all() and (xq[2] == -127).all()
+    for eps in (1e-6, 0.0):
+        xq, beta, normed = oracle.rmsnorm_act_quant(x, w, eps, want_normed=True)
+        # zero row (also at eps = 0): n = 0, beta clamps, codes vanish
+        assert (normed[0] == 0).all() and beta[0] == np.float32(1e-5) and (xq[0] == 0).all()
+        # constant rows normalise to +-1 up to eps: every code is +-127
+        assert np.abs(np.abs(normed[1:]) - 1).max() < 1e-5
+        assert (xq[1] == 127).all() and (xq[2] == -127).all()
+
+
+def test_rmsnorm_extreme_magnitudes_stay_normalised():
+    """Rows near the top and bottom of the bf16 range: mean(x^2) leaves the
+    float range, but the double evaluation still normalises them (the
+    result matches the float64 statement)."""
+    K = 128
+    base = synth.rng("test/rms/extreme").standard_normal(K).astype(np.float32)
+    w = np.ones(K, dtype=np.float32)
+    for scale in (1e30, 1e-30):
+        x = synth.float_to_bf16_bits((base * np.float32(scale))[None, :])
+        xq, beta, normed = oracle.rmsnorm_act_quant(x, w, 0.0, want_normed=True)
+        xf = _bf16_to_f32(x).astype(np.float64)
+        ref = xf / np.sqrt((xf * xf).mean())
+        assert np.abs(normed - ref).max() < 1e-6 * np.abs(ref).max()
+        assert np.abs(xq).max() == 127
 
 
 # ------------------------------------------------------------- mask stats
