@@ -422,6 +422,58 @@ def secondary(torch, sbl, synth, dev, timer):
     del jobs
     torch.cuda.empty_cache()
 
+    # ---- operators around the path: RMSNorm -> int8, mask monitor,
+    #      per-tensor absmean, on the 0.5B layer's shapes ----
+    log("[bench] RMSNorm / mask monitor / per-tensor scale")
+    T = synth.QWEN05B_PREFILL_TOKENS
+    nxt = {}
+    rms = {}
+    for K in (896, 4864):
+        xb = torch.from_numpy(synth.activations_bf16(f"cfg2/rms/x/{K}", T, K).view(np.int16)).to(dev)
+        wn = torch.from_numpy(synth.norm_weight(f"cfg2/rms/w/{K}", K)).to(dev)
+        xq_o = torch.empty((T, K), dtype=torch.int8, device=dev)
+        b_o = torch.empty(T, dtype=torch.float32, device=dev)
+        ur = graph_time(torch, [lambda: sbl.rmsnorm_act_quant_i8(xb, wn, 1e-6, xq_o, b_o)], reps=30)
+        ua = graph_time(torch, [lambda: sbl.act_quant_i8(xb, xq_o, b_o)], reps=30)
+        byts = 3.0 * T * K + 4 * T
+        rms[f"K{K}"] = {"us": round(ur, 2), "gbs": round(byts / (ur * 1e-6) / 1e9, 1),
+                        "frac_hbm": round(byts / (ur * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                        "act_quant_alone_us": round(ua, 2)}
+        del xb, xq_o
+    nxt["rmsnorm_act_quant_T32768"] = rms
+    # mask monitor over a bandwidth-sized input: the 16 gate masks of the
+    # 2048/7168 stack, stacked row-wise (one flat bit stream), against the
+    # masks of the same weights after a small update
+    rows_m, cols_m = 16 * 7168, 2048
+    Wm = torch.from_numpy(synth.latent_weight("cfg5/stack/gate/W", rows_m, cols_m)).to(dev)
+    ma = sbl.nm_mask_create(Wm, 3, 4)
+    Wm.add_(1e-4 * torch.randn_like(Wm))
+    mb = sbl.nm_mask_create(Wm, 3, 4)
+    del Wm
+    st = torch.empty(2, dtype=torch.int64, device=dev)
+    _, mm = timer.time(lambda i=0: sbl.nm_mask_stats(ma, mb, rows_m, cols_m, 3, 4, st), 20)
+    mbytes = 2.0 * rows_m * cols_m / 8
+    torch.cuda.synchronize()
+    nxt["mask_stats_wide_gate_stack_3of4"] = {
+        "weights": rows_m * cols_m, "us": round(mm * 1e3, 2),
+        "gbs": round(mbytes / (mm * 1e-3) / 1e9, 1),
+        "frac_hbm": round(mbytes / (mm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "changed_frac": round(int(st[0]) / (rows_m * cols_m), 6), "bad_groups": int(st[1])}
+    del ma, mb
+    # per-tensor absmean refresh of the gate matrix (reads W twice)
+    Wg = torch.from_numpy(synth.latent_weight("cfg2/L0/gate/W", 4864, 896)).to(dev)
+    outs = sbl.nm_mask_quant_pack(Wg, 3, 4, sbl.SCALE_PER_TENSOR, want_mask=False)
+    up = graph_time(torch, [lambda: sbl.nm_mask_quant_pack(Wg, 3, 4, sbl.SCALE_PER_TENSOR, out=outs)], reps=50)
+    uq = graph_time(torch, [lambda: sbl.nm_mask_quant_pack(Wg, 3, 4, 0, out=outs)], reps=50)
+    nw = 4864 * 896
+    nxt["per_tensor_refresh_gate_4864x896"] = {
+        "us": round(up, 2), "gbs": round(8.25 * nw / (up * 1e-6) / 1e9, 1),
+        "per_row_us": round(uq, 2), "per_row_gbs": round(4.25 * nw / (uq * 1e-6) / 1e9, 1)}
+    res["next_rows"] = nxt
+    log(f"[bench] next rows: {nxt}")
+    del Wg
+    torch.cuda.empty_cache()
+
     # ---- tiny 256 -> 512 layer: the whole pipeline ----
     Wt = torch.from_numpy(synth.latent_weight("cfg1/W", 512, 256)).to(dev)
     xt = torch.from_numpy(synth.activations_bf16("cfg1/x", 128, 256).view(np.int16)).to(dev)
@@ -434,8 +486,8 @@ def secondary(torch, sbl, synth, dev, timer):
         sbl.act_quant_i8(xt, xqt, bt)
         sbl.sparse_bitlinear_gemm(xqt, bt, outs[1], outs[2], y=yt)
 
-    _, mt = timer.time(tiny, 50)
-    res["tiny_256x512_T128"] = {"pipeline_us": round(mt * 1e3, 2)}
+    res["tiny_256x512_T128"] = {"pipeline_us": round(graph_time(torch, [tiny], reps=50), 2),
+                                "pipeline_eager_us": round(timer.time(tiny, 50)[1] * 1e3, 2)}
     return res
 
 

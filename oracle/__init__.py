@@ -43,6 +43,11 @@ something other than itself; the tests named are under ``tests/``):
                      (test_oracle_next.py).
 * ``tensor_scale``   exact rational mean over the tensor rounded to float;
                      one-row tensors equal ``row_scale`` (test_oracle_next.py).
+* ``ste_backward``   exact rational sums on tiny shapes; numpy float64
+                     matmul of the same float factors; linearity of the
+                     forward (the change of sum(dy * y) for a one-step change
+                     of a code or of x~, through gemm_acc) equals the
+                     gradient entry (test_oracle_ste.py).
 * ``dequant``        exact rational product rounded to float
                      (test_oracle_gemm.py); whole-layer cross-check against
                      a float64 re-statement of the guide's PyTorch module with
@@ -108,6 +113,7 @@ def _load():
     lib.oracle_mask_stats.argtypes = [P, P, I64, I64, I, I, P]
     lib.oracle_tensor_scale.argtypes = [P, P, I, I64, I64]
     lib.oracle_tensor_scale.restype = ctypes.c_float
+    lib.oracle_ste_backward.argtypes = [P, P, P, P, P, I64, I64, I64, P, P]
     lib.oracle_bf16_rne.argtypes = [ctypes.c_float]
     lib.oracle_bf16_rne.restype = ctypes.c_uint16
     lib.oracle_num_threads.argtypes = []
@@ -260,6 +266,26 @@ def tensor_scale(W: np.ndarray, mask_bits: np.ndarray | None = None,
         mask_bits = _c(mask_bits, np.uint8)
     return np.float32(_load().oracle_tensor_scale(_ptr(W), _ptr(mask_bits) if from_masked else None,
                                                   1 if from_masked else 0, rows, cols))
+
+
+def ste_backward(dy: np.ndarray, xq: np.ndarray, beta: np.ndarray, codes: np.ndarray,
+                 gamma: np.ndarray, want_dx: bool = True, want_dw: bool = True):
+    """Straight-through backward of the layer: dy fp32 [T, N], x~ int8
+    [T, K], beta fp32 [T], codes int8 [N, K], gamma fp32 [N] ->
+    (dx fp32 [T, K] or None, dw fp32 [N, K] or None)."""
+    dy = _c(dy, np.float32)
+    xq = _c(xq, np.int8)
+    beta = _c(beta, np.float32)
+    codes = _c(codes, np.int8)
+    gamma = _c(gamma, np.float32)
+    T, N = dy.shape
+    N2, K = codes.shape
+    assert N2 == N and xq.shape == (T, K) and beta.shape == (T,) and gamma.shape == (N,)
+    dx = np.empty((T, K), dtype=np.float32) if want_dx else None
+    dw = np.empty((N, K), dtype=np.float32) if want_dw else None
+    _load().oracle_ste_backward(_ptr(dy), _ptr(xq), _ptr(beta), _ptr(codes), _ptr(gamma),
+                                T, K, N, _ptr(dx), _ptr(dw))
+    return dx, dw
 
 
 def bf16_rne(f: float) -> int:

@@ -353,6 +353,60 @@ float oracle_tensor_scale(const float* W, const uint8_t* mask_bits, int from_mas
   return g;
 }
 
+/* ------------------------------------------------------------------------ *
+ * Backward pass with the straight-through estimator.
+ * [guide] "Training Stability & The Straight-Through Estimator": gradients
+ * pass through the 2:4 mask and the ternary rounding unchanged to the
+ * latent weights (dL/dW = dL/dW~); the module's backward returns the
+ * gradient of the sparse ternary weight as the weight gradient.  [repo]
+ * "BitLinear": gradients flow through by STE.
+ *
+ * With y[t,o] = acc[t,o] * beta_t * gamma_o / 127 and acc = x~ . W~^T, and
+ * dy the gradient of the loss with respect to y:
+ *   dw[o,k] = gamma_o * sum_t (dy[t,o] * (beta_t/127)) * x~[t,k]
+ *             (the exact gradient with respect to W~, passed straight to W)
+ *   dx[t,k] = sum_o (dy[t,o] * gamma_o) * code[o,k]
+ *             (reading: the activation quantiser is passed straight
+ *             through as well, x~ * beta / 127 standing in for x; the guide's
+ *             module rounds without an estimator, which would give 0)
+ * Reading of the precision: the scaled factors dy*gamma, beta/127 and
+ * dy*(beta/127) are float products / quotients (one rounding each), the
+ * sums are exact real sums (here double, one rounding to float), and dw's
+ * final product with gamma is one float multiply.  dx or dw may be NULL.
+ * ------------------------------------------------------------------------ */
+void oracle_ste_backward(const float* dy, const int8_t* xq, const float* beta,
+                         const int8_t* codes, const float* gamma, int64_t T, int64_t K,
+                         int64_t N, float* dx, float* dw) {
+  if (dx) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      for (int64_t k = 0; k < K; ++k) {
+        double s = 0.0;
+        for (int64_t o = 0; o < N; ++o) {
+          int8_t c = codes[o * K + k];
+          if (c == 0) continue;
+          float a = dy[t * N + o] * gamma[o];
+          s += c > 0 ? (double)a : -(double)a;
+        }
+        dx[t * K + k] = (float)s;
+      }
+    }
+  }
+  if (dw) {
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < N; ++o) {
+      for (int64_t k = 0; k < K; ++k) {
+        double s = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+          float b = dy[t * N + o] * (beta[t] / 127.0f);
+          s += (double)b * (double)xq[t * K + k];
+        }
+        dw[o * K + k] = (float)s * gamma[o];
+      }
+    }
+  }
+}
+
 /* Number of OpenMP threads the oracle runs with (1 when built without it). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -57,6 +57,13 @@ def norm_weight(tag: str, cols: int) -> np.ndarray:
             * np.float32(0.1)).astype(np.float32)
 
 
+def grad_output(tag: str, tokens: int, cols: int) -> np.ndarray:
+    """float32 [tokens, cols] ~ N(0, 1e-3): a stand-in for the gradient of
+    the loss with respect to a layer's output."""
+    return (rng(tag).standard_normal((tokens, cols), dtype=np.float32)
+            * np.float32(1e-3)).astype(np.float32)
+
+
 def mask_flip(tag: str, mask_bits: np.ndarray, fraction: float) -> np.ndarray:
     """A copy of a bit-packed mask with about `fraction` of its bits
     flipped at random (input generation for the mask-monitor tests)."""
