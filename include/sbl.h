@@ -272,6 +272,45 @@ int sparse_bitlinear_gemv_grouped(const sbl_gemv_desc* descs_host,
                                   const sbl_gemv_desc* descs_dev, int count,
                                   int64_t T, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Backward pass with the straight-through estimator (training).
+ * Guide "Training Stability & The Straight-Through Estimator" (the gradient
+ * passes through the mask and the ternary rounding to the latent weights)
+ * and its module's backward; README "BitLinear" (gradients flow through by
+ * STE).  With dy = dL/dy [T, N] of y = acc * beta * gamma / 127:
+ *   dw[o,k] = gamma_o * sum_t (dy[t,o] * (beta_t/127)) * x~[t,k]
+ *             (dL/dW~, passed straight to the latent weight W)
+ *   dx[t,k] = sum_o (dy[t,o] * gamma_o) * code[o,k]
+ *             (the activation quantiser passed straight through:
+ *             x~ * beta/127 stands for x)
+ * dy*gamma, beta/127 and dy*(beta/127) are float operations; the sums are
+ * accumulated in float on bf16 matrix cores from an exact three-piece bf16
+ * split of the float factor (every product exact).  A matrix-core step adds
+ * 16 exact products of one piece to the accumulator, three steps per 16
+ * terms; dw adds at most 32 partial sums in a fixed order and then rounds
+ * the product with gamma.  With one rounding per step, each entry is within
+ * (3R/16 + 36) * 2^-24 * sum|terms| of the exact sum (R the reduction
+ * length: N for dx, T for dw).
+ *   dy       float [T, N]
+ *   xq, beta int8 [T, K], float [T]            (needed for dw)
+ *   packed   uint8 [N, K/4]                    (needed for dx)
+ *   row_scale float [N]
+ *   dx       float [T, K] or NULL;  dw  float [N, K] or NULL
+ *   workspace  device memory of at least
+ *              sparse_bitlinear_ste_workspace_bytes(T, K, N) bytes when dw is
+ *              requested (the token reduction of dw is split across the GPU
+ *              and its partial sums are added in a fixed order); NULL when
+ *              that size is 0 or dw is NULL
+ * An empty reduction (N = 0 for dx, T = 0 for dw) writes zeros; the
+ * operands it would read may then be NULL.
+ * Errors: SBL_ERR_ARG also for a workspace smaller than required.
+ * ------------------------------------------------------------------------ */
+size_t sparse_bitlinear_ste_workspace_bytes(int64_t T, int64_t K, int64_t N);
+int sparse_bitlinear_ste_backward(const float* dy, const int8_t* xq, const float* beta,
+                                  const uint8_t* packed, const float* row_scale, int64_t T,
+                                  int64_t K, int64_t N, float* dx, float* dw, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,8 @@ __all__ = [
     "sparse_bitlinear_gemm_sparse24", "sparse_bitlinear_gemv",
     "sparse_bitlinear_gemv_grouped", "GemvDesc", "RefreshDesc", "refresh_descs", "gemv_descs",
     "SCALE_FROM_MASKED", "SCALE_PER_TENSOR", "SCALE_F32", "SCALE_BF16", "GEMV_MAX_TOKENS",
-    "rmsnorm_act_quant_i8", "nm_mask_stats",
+    "rmsnorm_act_quant_i8", "nm_mask_stats", "sparse_bitlinear_ste_backward",
+    "sparse_bitlinear_ste_workspace_bytes",
 ]
 
 SCALE_FROM_MASKED = 1
@@ -85,6 +86,8 @@ def load() -> ctypes.CDLL:
         "act_quant_i8": [P, I64, I64, P, P, P],
         "rmsnorm_act_quant_i8": [P, P, ctypes.c_float, I64, I64, P, P, P],
         "nm_mask_stats": [P, P, I64, I64, I, I, P, P],
+        "sparse_bitlinear_ste_backward": [P, P, P, P, P, I64, I64, I64, P, P, P,
+                                          ctypes.c_size_t, P],
         "sparse_bitlinear_gemm": [P, P, P, P, I, I64, I64, I64, P, P, P],
         "sparse24_compress": [P, I64, I64, P, P, P],
         "sparse_bitlinear_gemm_sparse24": [P, P, P, P, I, I64, I64, I64, P, P, P],
@@ -95,6 +98,8 @@ def load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = ctypes.c_int
+    lib.sparse_bitlinear_ste_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.sparse_bitlinear_ste_workspace_bytes.restype = ctypes.c_size_t
     lib.sparse24_bytes.argtypes = [I64, I64]
     lib.sparse24_bytes.restype = ctypes.c_size_t
     lib.sbl_status_str.argtypes = [I]
@@ -271,6 +276,39 @@ def nm_mask_stats(old_bits: torch.Tensor | None, new_bits: torch.Tensor, rows: i
     _check("nm_mask_stats", load().nm_mask_stats(
         _ptr(old_bits), _ptr(new_bits), rows, cols, n, m, _ptr(stats), _stream(new_bits.device)))
     return stats
+
+
+def sparse_bitlinear_ste_workspace_bytes(T: int, K: int, N: int) -> int:
+    return int(load().sparse_bitlinear_ste_workspace_bytes(T, K, N))
+
+
+def sparse_bitlinear_ste_backward(dy, xq, beta, packed, scale, want_dx: bool = True,
+                                  want_dw: bool = True, workspace: torch.Tensor | None = None):
+    """Straight-through backward: dy float32 [T, N], xq int8 [T, K], beta
+    float32 [T], packed uint8 [N, K/4], scale float32 [N] -> (dx float32
+    [T, K] or None, dw float32 [N, K] or None).  `workspace` (uint8 device
+    tensor) is allocated here when not given."""
+    _need(dy, torch.float32, "dy", 2)
+    _need(xq, torch.int8, "xq", 2)
+    _need(packed, torch.uint8, "packed", 2)
+    T, N = dy.shape
+    K = xq.shape[1]
+    _shape(xq, (T, K), torch.int8, "xq")
+    _shape(beta, (T,), torch.float32, "beta")
+    _shape(packed, (N, K // 4), torch.uint8, "packed")
+    _shape(scale, (N,), torch.float32, "scale")
+    dev = dy.device
+    dx = torch.empty((T, K), dtype=torch.float32, device=dev) if want_dx else None
+    dw = torch.empty((N, K), dtype=torch.float32, device=dev) if want_dw else None
+    need = sparse_bitlinear_ste_workspace_bytes(T, K, N) if want_dw else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace", 1)
+    _check("sparse_bitlinear_ste_backward", load().sparse_bitlinear_ste_backward(
+        _ptr(dy), _ptr(xq), _ptr(beta), _ptr(packed), _ptr(scale), T, K, N, _ptr(dx), _ptr(dw),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)))
+    return dx, dw
 
 
 def act_quant_i8(x: torch.Tensor, xq: torch.Tensor | None = None,

@@ -237,4 +237,34 @@ int sparse_bitlinear_gemv_grouped(const sbl_gemv_desc* descs_host, const sbl_gem
   return hip_status(sbl::launch_gemv(descs_host, descs_dev, count, T, stream));
 }
 
+size_t sparse_bitlinear_ste_workspace_bytes(int64_t T, int64_t K, int64_t N) {
+  if (T <= 0 || N <= 0 || check_cols(K) != SBL_OK) return 0;
+  return sbl::ste_workspace_bytes(T, K, N);
+}
+
+int sparse_bitlinear_ste_backward(const float* dy, const int8_t* xq, const float* beta,
+                                  const uint8_t* packed, const float* row_scale, int64_t T,
+                                  int64_t K, int64_t N, float* dx, float* dw, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || N < 0 || T > kMaxRows || N > kMaxRows) return SBL_ERR_ARG;
+  if (int s = check_cols(K)) return s;
+  if (T == 0) dx = nullptr;  // empty outputs
+  if (N == 0) dw = nullptr;
+  if (!dx && !dw) return SBL_OK;
+  const bool reads = T > 0 && N > 0;  // otherwise the reduction is empty: zeros
+  if (reads && !dy) return SBL_ERR_ARG;
+  if (N > 0 && !row_scale) return SBL_ERR_ARG;
+  if (dx && reads && !packed) return SBL_ERR_ARG;
+  if (dw && reads && (!xq || !beta)) return SBL_ERR_ARG;
+  const size_t need = dw ? sbl::ste_workspace_bytes(T, K, N) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SBL_ERR_ARG;
+  if (!aligned16_or_null(dy) || !aligned16_or_null(row_scale) || !aligned16_or_null(xq) ||
+      !aligned16_or_null(beta) || !aligned16_or_null(packed) || !aligned16_or_null(dx) ||
+      !aligned16_or_null(dw) || (need > 0 && !aligned16(workspace)))
+    return SBL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(sbl::launch_ste_backward(dy, xq, beta, packed, row_scale, T, K, N, dx, dw,
+                                             need > 0 ? workspace : nullptr, stream));
+}
+
 }  // extern "C"

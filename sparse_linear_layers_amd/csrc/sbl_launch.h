@@ -39,6 +39,11 @@ hipError_t launch_sparse24_compress(const uint8_t* packed, int64_t N, int64_t K,
 hipError_t launch_gemm_sparse24(const int8_t* xq, const float* beta, const void* sp,
                                 const void* scale, int scale_bf16, int64_t T, int64_t K, int64_t N,
                                 float* y, int32_t* acc, hipStream_t stream);
+size_t ste_workspace_bytes(int64_t T, int64_t K, int64_t N);
+hipError_t launch_ste_backward(const float* dy, const int8_t* xq, const float* beta,
+                               const uint8_t* packed, const float* gamma, int64_t T, int64_t K,
+                               int64_t N, float* dx, float* dw, void* workspace,
+                               hipStream_t stream);
 int64_t gemv_blocks(int64_t N, int64_t T);  // blocks of the decode product over N rows
 hipError_t launch_gemv(const sbl_gemv_desc* host, const sbl_gemv_desc* dev_or_null, int count,
                        int64_t T, hipStream_t stream);

@@ -156,3 +156,26 @@ def test_per_tensor_flag(lib):
     # the grouped refresh keeps per-row scales only
     g = lib.nm_mask_quant_pack_grouped
     assert g(P, P, 1, 3, 4, 2, None) == UNSUP
+
+
+def test_ste_backward_validation(lib):
+    f = lib.sparse_bitlinear_ste_backward
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 3 + \
+        [ctypes.c_size_t, ctypes.c_void_p]
+    wsb = lib.sparse_bitlinear_ste_workspace_bytes
+    wsb.argtypes = [ctypes.c_int64] * 3
+    wsb.restype = ctypes.c_size_t
+    need = wsb(32768, 896, 896)
+    assert need > 0 and wsb(0, 896, 896) == 0 and wsb(16, 100, 16) == 0
+    # nothing requested / empty: no-op
+    assert f(P, P, P, P, P, 64, 128, 64, None, None, None, 0, None) == OK
+    assert f(P, P, P, P, P, 0, 128, 64, P, None, None, 0, None) == OK   # empty dx
+    assert f(P, P, P, P, P, 64, 128, 0, None, P, None, 0, None) == OK   # empty dw
+    assert f(None, None, None, None, None, 0, 128, 64, None, P, None, 0, None) == ARG  # gamma
+    assert f(None, P, P, P, P, 64, 128, 64, P, None, None, 0, None) == ARG
+    assert f(P, P, P, None, P, 64, 128, 64, P, None, None, 0, None) == ARG     # dx needs codes
+    assert f(P, None, P, P, P, 64, 128, 64, None, P, P, 1 << 30, None) == ARG  # dw needs x~
+    assert f(P, P, P, P, P, 32768, 896, 896, None, P, P, need - 1, None) == ARG  # small workspace
+    assert f(P, P, P, P, P, 32768, 896, 896, None, P, None, need, None) == ARG
+    assert f(P, P, P, P, P, 64, 100, 64, P, None, None, 0, None) == SHAPE
+    assert f(MIS, P, P, P, P, 64, 128, 64, P, None, None, 0, None) == ALIGN

@@ -163,3 +163,88 @@ def test_per_tensor_full_size_matrix(sbl):
     y, acc = sbl.sparse_bitlinear_gemm(dev(xq), dev(beta), packed, scale, want_acc=True)
     codes = oracle.unpack_codes(packed_ref, 896)
     assert np.array_equal(host(acc), oracle.gemm_acc(xq, codes))
+
+
+# ------------------------------------------------------ STE backward
+def _ste_operands(tag, T, K, N):
+    W = synth.latent_weight(f"{tag}/W", N, K)
+    x = synth.activations_bf16(f"{tag}/x", T, K)
+    mask = oracle.nm_mask(W, 3, 4)
+    g, _ = oracle.row_scale(W)
+    codes = oracle.ternary_codes(W, mask, g)
+    xq, beta = oracle.act_quant(x)
+    dy = synth.grad_output(f"{tag}/dy", T, N)
+    return dict(codes=codes, packed=oracle.pack_codes(codes), g=g, xq=xq, beta=beta, dy=dy)
+
+
+def _ste_bounds(o, rows=None, cols=None):
+    """Per-entry error bounds of dx[rows] and dw[:, cols]: float
+    accumulation of R exact products in 16-term matrix-core steps, three
+    per 16 terms (one per bf16 piece), at most 32 partial sums and the
+    final product with gamma: (3R/16 + 36) * 2^-24 * sum|terms|."""
+    dy, g = o["dy"], o["g"]
+    T, N = dy.shape
+    dyr = dy if rows is None else dy[rows]
+    a = np.abs((dyr * g[None, :]).astype(np.float32)).astype(np.float64)
+    s = (o["beta"] / np.float32(127)).astype(np.float32)
+    b = np.abs((dy * s[:, None]).astype(np.float32)).astype(np.float64)
+    xq = o["xq"] if cols is None else o["xq"][:, cols]
+    sdx = a @ np.abs(o["codes"]).astype(np.float64)
+    sdw = (b.T @ np.abs(xq).astype(np.float64)) * g[:, None].astype(np.float64)
+    u = 2.0 ** -24
+    return (3 * N / 16 + 36) * u * sdx + 1e-37, (3 * T / 16 + 36) * u * sdw + 1e-37
+
+
+@pytest.mark.parametrize("T,K,N", [(128, 256, 512), (300, 896, 200), (33, 64, 4), (1, 64, 1),
+                                   (129, 4864, 260), (1000, 192, 130), (2048, 896, 128),
+                                   (4100, 320, 96)])
+def test_ste_backward(sbl, T, K, N):
+    o = _ste_operands(f"gpu/ste/{T}x{K}x{N}", T, K, N)
+    dx_ref, dw_ref = oracle.ste_backward(o["dy"], o["xq"], o["beta"], o["codes"], o["g"])
+    args = [dev(o[k]) for k in ("dy", "xq", "beta", "packed", "g")]
+    dx, dw = sbl.sparse_bitlinear_ste_backward(*args)
+    bdx, bdw = _ste_bounds(o)
+    assert (np.abs(host(dx).astype(np.float64) - dx_ref) <= bdx).all()
+    assert (np.abs(host(dw).astype(np.float64) - dw_ref) <= bdw).all()
+    # each output alone, and a caller workspace full of stale values: the
+    # same bits (the reduction order is fixed)
+    dx2, none = sbl.sparse_bitlinear_ste_backward(*args, want_dw=False)
+    need = sbl.sparse_bitlinear_ste_workspace_bytes(T, K, N)
+    ws = torch.full((max(need, 16),), 0x7f, dtype=torch.uint8, device=DEV)
+    none2, dw2 = sbl.sparse_bitlinear_ste_backward(*args, want_dx=False, workspace=ws)
+    assert none is None and none2 is None
+    assert torch.equal(dx, dx2) and torch.equal(dw, dw2)
+
+
+def test_ste_backward_empty_reductions(sbl):
+    """No tokens: dw is a sum over nothing (zeros); no output rows: dx is."""
+    K, N = 192, 40
+    o = _ste_operands("gpu/ste/empty", 8, K, N)
+    e = lambda *s: torch.empty(s, dtype=torch.float32, device=DEV)
+    got = sbl.sparse_bitlinear_ste_backward(e(0, N), torch.empty((0, K), dtype=torch.int8, device=DEV),
+                                            e(0), dev(o["packed"]), dev(o["g"]))
+    assert got[0].shape == (0, K) and (host(got[1]) == 0).all()
+    got = sbl.sparse_bitlinear_ste_backward(e(8, 0), dev(o["xq"]), dev(o["beta"]),
+                                            torch.empty((0, K // 4), dtype=torch.uint8, device=DEV),
+                                            e(0))
+    assert (host(got[0]) == 0).all() and got[1].shape == (0, K)
+
+
+def test_ste_backward_full_size_sampled(sbl):
+    """The 0.5B skeleton's gate linear at 32768 tokens: dx on sampled token
+    rows, dw on sampled input columns (each depends only on its own
+    slice), against the oracle."""
+    T, K, N = synth.QWEN05B_PREFILL_TOKENS, 896, 4864
+    o = _ste_operands("gpu/ste/full/gate", T, K, N)
+    dx, dw = sbl.sparse_bitlinear_ste_backward(dev(o["dy"]), dev(o["xq"]), dev(o["beta"]),
+                                               dev(o["packed"]), dev(o["g"]))
+    pick = synth.rng("gpu/ste/full/pick")
+    rows = np.unique(np.concatenate([[0, T - 1], pick.choice(T, 62, replace=False)]))
+    cols = np.unique(np.concatenate([[0, K - 1], pick.choice(K, 30, replace=False)]))
+    dx_ref, _ = oracle.ste_backward(o["dy"][rows], o["xq"][rows], o["beta"][rows], o["codes"],
+                                    o["g"], want_dw=False)
+    _, dw_ref = oracle.ste_backward(o["dy"], o["xq"][:, cols], o["beta"], o["codes"][:, cols],
+                                    o["g"], want_dx=False)
+    bdx, bdw = _ste_bounds(o, rows=rows, cols=cols)
+    assert (np.abs(host(dx)[rows].astype(np.float64) - dx_ref) <= bdx).all()
+    assert (np.abs(host(dw)[:, cols].astype(np.float64) - dw_ref) <= bdw).all()
