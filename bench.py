@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PEAK_I8_TOPS = 5000.0      # MI355X dense int8 matrix peak (5.0 POP/s)
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (2.5 PFLOP/s)
 METRIC = "Sparse-BitLinear int8 TOPS (prefill) + HBM GB/s (decode), 3:4 @ d896/ffn4864"
 
 
@@ -469,6 +470,30 @@ def secondary(torch, sbl, synth, dev, timer):
     nxt["per_tensor_refresh_gate_4864x896"] = {
         "us": round(up, 2), "gbs": round(8.25 * nw / (up * 1e-6) / 1e9, 1),
         "per_row_us": round(uq, 2), "per_row_gbs": round(4.25 * nw / (uq * 1e-6) / 1e9, 1)}
+    # straight-through backward of the gate and down linears at 32768
+    # tokens: dx and dw separately (each is 2*T*N*K float products; the
+    # matrix cores run three bf16 pieces of each)
+    ste = {}
+    for name, N, K in (("gate", 4864, 896), ("down", 896, 4864)):
+        Wl = torch.from_numpy(synth.latent_weight(f"cfg2/L0/{name}/W", N, K)).to(dev)
+        _, pk, sc, _ = sbl.nm_mask_quant_pack(Wl, 3, 4)
+        del Wl
+        xb = torch.from_numpy(synth.activations_bf16(f"cfg2/ste/x/{K}", T, K).view(np.int16)).to(dev)
+        xqs, bs = sbl.act_quant_i8(xb)
+        del xb
+        dy = torch.from_numpy(synth.grad_output(f"cfg2/ste/dy/{N}", T, N)).to(dev)
+        ws = torch.empty(max(16, sbl.sparse_bitlinear_ste_workspace_bytes(T, K, N)),
+                         dtype=torch.uint8, device=dev)
+        _, mdx = timer.time(lambda i=0: sbl.sparse_bitlinear_ste_backward(dy, xqs, bs, pk, sc, want_dw=False), 10)
+        _, mdw = timer.time(lambda i=0: sbl.sparse_bitlinear_ste_backward(dy, xqs, bs, pk, sc, want_dx=False,
+                                                                          workspace=ws), 10)
+        fl = 2.0 * T * N * K
+        ste[f"{name}_{N}x{K}"] = {
+            "dx_us": round(mdx * 1e3, 1), "dw_us": round(mdw * 1e3, 1),
+            "dx_tflops": round(fl / (mdx * 1e-3) / 1e12, 1), "dw_tflops": round(fl / (mdw * 1e-3) / 1e12, 1),
+            "frac_bf16_mfma_peak": round(3 * 2 * fl / ((mdx + mdw) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del dy, xqs, ws
+    nxt["ste_backward_T32768"] = ste
     res["next_rows"] = nxt
     log(f"[bench] next rows: {nxt}")
     del Wg

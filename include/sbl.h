@@ -296,14 +296,16 @@ int sparse_bitlinear_gemv_grouped(const sbl_gemv_desc* descs_host,
  *   packed   uint8 [N, K/4]                    (needed for dx)
  *   row_scale float [N]
  *   dx       float [T, K] or NULL;  dw  float [N, K] or NULL
- *   workspace  device memory of at least
+ *   workspace  16-byte aligned device memory of at least
  *              sparse_bitlinear_ste_workspace_bytes(T, K, N) bytes when dw is
- *              requested (the token reduction of dw is split across the GPU
- *              and its partial sums are added in a fixed order); NULL when
- *              that size is 0 or dw is NULL
+ *              requested (it holds beta/127 per token and, when the token
+ *              reduction of dw is split across the GPU, the partial sums,
+ *              added afterwards in a fixed order); NULL when that size is 0
+ *              or dw is NULL.  Its contents on entry do not matter.
  * An empty reduction (N = 0 for dx, T = 0 for dw) writes zeros; the
  * operands it would read may then be NULL.
- * Errors: SBL_ERR_ARG also for a workspace smaller than required.
+ * Errors: SBL_ERR_ARG also for a workspace smaller than required;
+ * SBL_ERR_SHAPE for N > 2^22 or K outside the column limits.
  * ------------------------------------------------------------------------ */
 size_t sparse_bitlinear_ste_workspace_bytes(int64_t T, int64_t K, int64_t N);
 int sparse_bitlinear_ste_backward(const float* dy, const int8_t* xq, const float* beta,

@@ -248,6 +248,7 @@ int sparse_bitlinear_ste_backward(const float* dy, const int8_t* xq, const float
                                   size_t workspace_bytes, hipStream_t stream) {
   if (T < 0 || N < 0 || T > kMaxRows || N > kMaxRows) return SBL_ERR_ARG;
   if (int s = check_cols(K)) return s;
+  if (N > (int64_t(1) << 22)) return SBL_ERR_SHAPE;  // 32-bit per-lane offsets into dy tiles
   if (T == 0) dx = nullptr;  // empty outputs
   if (N == 0) dw = nullptr;
   if (!dx && !dw) return SBL_OK;

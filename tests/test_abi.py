@@ -166,7 +166,8 @@ def test_ste_backward_validation(lib):
     wsb.argtypes = [ctypes.c_int64] * 3
     wsb.restype = ctypes.c_size_t
     need = wsb(32768, 896, 896)
-    assert need > 0 and wsb(0, 896, 896) == 0 and wsb(16, 100, 16) == 0
+    assert need > 0 and wsb(0, 896, 896) == 0 and wsb(16, 128, 16) == 64   # 16 token scales
+    assert f(P, P, P, P, P, 64, 128, (1 << 22) + 1, P, None, None, 0, None) == SHAPE
     # nothing requested / empty: no-op
     assert f(P, P, P, P, P, 64, 128, 64, None, None, None, 0, None) == OK
     assert f(P, P, P, P, P, 0, 128, 64, P, None, None, 0, None) == OK   # empty dx
