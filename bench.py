@@ -219,8 +219,9 @@ def main():
         tot_ops += ops
     gemm_tops = tot_ops / (tot_ms * 1e-3) / 1e12
     sha = kernel_sha("gemm.hip", "sbl_device.h")
-    tr = load_traffic("gemm_i8_kernel", sha)
-    roofline = {"kernel": "gemm_i8_kernel (7 prefill products of the layer, mean per launch)",
+    tr = load_traffic("prefill_products", sha)
+    roofline = {"kernel": "prefill products, mean per launch over the layer's 7: gemm_i8_ws_kernel "
+                          "(q/o/gate/up/down) and gemm_i8_kernel<128,128,2> (k/v: too few 256x256 tiles)",
                 "bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_I8_TOPS,
                 "unit": "TFLOP/s", "op": "int8 ops (2*T*N*K, dense-equivalent)",
                 "frac": round(gemm_tops / PEAK_I8_TOPS, 4),
