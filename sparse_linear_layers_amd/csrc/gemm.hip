@@ -560,12 +560,17 @@ __global__ __launch_bounds__(ws::NT, 1) void gemm_i8_ws_kernel(GemmArgs a) {
     SBL_LOAD(1);
     SBL_LOAD(0);
     __syncthreads();
+    // The empty asm statements keep the compiler from sinking a step's loads
+    // past the barrier and the next write (which would shorten the prefetch
+    // distance to one step).
     for (int s = 0; s < total2; s += 2) {
       if (s + 1 < total) SBL_WRITE(1, 1);  // step s+1
       SBL_LOAD(1);                         // step s+3
+      __asm__ volatile("" ::: "memory");
       __syncthreads();
       if (s + 2 < total) SBL_WRITE(0, 0);  // step s+2
       SBL_LOAD(0);                         // step s+4
+      __asm__ volatile("" ::: "memory");
       __syncthreads();
     }
 #undef SBL_LOAD
