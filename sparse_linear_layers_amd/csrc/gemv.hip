@@ -156,40 +156,26 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void gemv_kernel(GemvArgs a, i
     const int K = dc.K, N = dc.N;
     const int64_t row0 = dc.row0;
 
-    float sc[E][4];
-    {
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(dc.row_scale), (short)0, N * (dc.bf16 ? 2 : 4), 0x00020000);
+    // Row scales of this lane's four rows per finished row group (rows past
+    // N clamped) and beta, loaded now and converted only at the epilogue, so
+    // that their memory round trip overlaps the code loads.  Both scale
+    // types are requested, the unused one at an offset past the buffer;
+    // every offset and the resource are uniform in structure, so no load
+    // sits behind a branch that would force an early wait.
+    const int bf16 = __builtin_amdgcn_readfirstlane(dc.bf16);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(dc.row_scale), (short)0, __builtin_amdgcn_readfirstlane(N << (bf16 ? 1 : 2)),
+        0x00020000);
+    uint32_t sh[E][4], sf[E][4];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        // four consecutive rows o..o+3 (o % 4 == 0, in bounds when o < N and
-        // N % 4 == 0); otherwise row by row, clamped
-        const int64_t o = row0 + 16 * (wave * E + e) + 4 * g;
-        if ((N & 3) == 0 && o < N) {
-          if (dc.bf16) {
-            const v2i h = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(2 * o), 0, 0);
-            sc[e][0] = __uint_as_float((uint32_t)h.x << 16);
-            sc[e][1] = __uint_as_float((uint32_t)h.x & 0xffff0000u);
-            sc[e][2] = __uint_as_float((uint32_t)h.y << 16);
-            sc[e][3] = __uint_as_float((uint32_t)h.y & 0xffff0000u);
-          } else {
-            const v4i f = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(4 * o), 0, 0);
-            sc[e][0] = __int_as_float(f.x);
-            sc[e][1] = __int_as_float(f.y);
-            sc[e][2] = __int_as_float(f.z);
-            sc[e][3] = __int_as_float(f.w);
-          }
-        } else {
+    for (int e = 0; e < E; ++e)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int oc = (int)min(o + r, (int64_t)N - 1);
-            sc[e][r] = dc.bf16 ? __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * oc, 0, 0) << 16)
-                               : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * oc, 0, 0));
-          }
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int oc = (int)min(row0 + 16 * (wave * E + e) + 4 * g + r, (int64_t)N - 1);
+        sh[e][r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(bf16 ? 2u * oc : kOut), 0, 0);
+        sf[e][r] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(bf16 ? kOut : 4u * oc), 0, 0);
       }
-    }
-    const float bt = __fdiv_rn(dc.beta[min(tok, T - 1)], 127.0f);
+    const float beta_raw = dc.beta[min(tok, T - 1)];
 
     int s_lo, s_hi;
     step_range(dc, s_lo, s_hi);
@@ -225,6 +211,7 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void gemv_kernel(GemvArgs a, i
       if (two) compute(w1, x1);
     }
 
+    const float bt = __fdiv_rn(beta_raw, 127.0f);
     // partial sums of the four K ranges
 #pragma unroll
     for (int rg = 0; rg < G; ++rg) sacc[wave][rg][lane] = acc[rg];
@@ -236,9 +223,12 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void gemv_kernel(GemvArgs a, i
       const v4i c = sacc[0][rg][lane] + sacc[1][rg][lane] + sacc[2][rg][lane] + sacc[3][rg][lane];
       const int64_t o = row0 + 16 * rg + 4 * g;
       if (tok_ok && o < N) {
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = bf16 ? __uint_as_float(sh[e][r] << 16) : __uint_as_float(sf[e][r]);
         float* yp = dc.y + (int64_t)tok * N + o;
-        const float v0 = ((float)c[0] * bt) * sc[e][0], v1 = ((float)c[1] * bt) * sc[e][1];
-        const float v2 = ((float)c[2] * bt) * sc[e][2], v3 = ((float)c[3] * bt) * sc[e][3];
+        const float v0 = ((float)c[0] * bt) * sc[0], v1 = ((float)c[1] * bt) * sc[1];
+        const float v2 = ((float)c[2] * bt) * sc[2], v3 = ((float)c[3] * bt) * sc[3];
         if ((N & 3) == 0) {  // o + 3 < N and 16-byte aligned
           *reinterpret_cast<float4*>(yp) = make_float4(v0, v1, v2, v3);
         } else {
