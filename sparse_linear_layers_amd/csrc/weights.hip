@@ -390,12 +390,17 @@ __device__ __forceinline__ uint32_t groups_not_n(uint32_t w, uint32_t n) {
   return (uint32_t)__popc(x);
 }
 
+// One block of 1024 threads per CU at most: few blocks keep the two 64-bit
+// atomics per block cheap (they serialise on one address), and four 16-byte
+// loads per operand and lane keep enough bytes in flight.
+constexpr int kStatsThreads = 1024;
+
 template <int M>
-__global__ __launch_bounds__(256) void mask_stats_kernel(const uint32_t* __restrict__ old_w,
-                                                         const uint32_t* __restrict__ new_w,
-                                                         int64_t words, int n,
-                                                         unsigned long long* stats) {
-  __shared__ uint32_t part[2][4];
+__global__ __launch_bounds__(kStatsThreads) void mask_stats_kernel(const uint32_t* __restrict__ old_w,
+                                                                   const uint32_t* __restrict__ new_w,
+                                                                   int64_t words, int n,
+                                                                   unsigned long long* stats) {
+  __shared__ unsigned long long part[2][kStatsThreads / kWave];
   uint32_t changed = 0, bad = 0;
   const int64_t nvec = words >> 2;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -404,33 +409,56 @@ __global__ __launch_bounds__(256) void mask_stats_kernel(const uint32_t* __restr
     changed += (uint32_t)__popc(a ^ b);
     bad += groups_not_n<M>(a, (uint32_t)n);
   };
-  for (int64_t i = gid; i < nvec; i += gsz) {
-    const uint4 a = reinterpret_cast<const uint4*>(new_w)[i];
-    const uint4 b = old_w ? reinterpret_cast<const uint4*>(old_w)[i] : a;
+  const uint4* nv = reinterpret_cast<const uint4*>(new_w);
+  const uint4* ov = reinterpret_cast<const uint4*>(old_w);
+  int64_t i = gid;
+  // four 16-byte loads per operand in flight per lane
+  for (; i + 3 * gsz < nvec; i += 4 * gsz) {
+    uint4 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = nv[i + u * gsz];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) b[u] = old_w ? ov[i + u * gsz] : a[u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      word(a[u].x, b[u].x);
+      word(a[u].y, b[u].y);
+      word(a[u].z, b[u].z);
+      word(a[u].w, b[u].w);
+    }
+  }
+  for (; i < nvec; i += gsz) {
+    const uint4 a = nv[i];
+    const uint4 b = old_w ? ov[i] : a;
     word(a.x, b.x);
     word(a.y, b.y);
     word(a.z, b.z);
     word(a.w, b.w);
   }
   for (int64_t i = 4 * nvec + gid; i < words; i += gsz) word(new_w[i], old_w ? old_w[i] : new_w[i]);
-  // per-block sums (each under 2^32 for any launch this library makes),
-  // then one 64-bit atomic per counter
+  // A lane's counts stay below 2^32 (at most 2^46 mask bits over 2^18
+  // lanes); wave and block sums are 64-bit, then one atomic per counter.
+  unsigned long long c64 = changed, g64 = bad;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
-    changed += (uint32_t)shfl_xor((int)changed, d);
-    bad += (uint32_t)shfl_xor((int)bad, d);
+    c64 += (unsigned long long)__shfl_xor((long long)c64, d, kWave);
+    g64 += (unsigned long long)__shfl_xor((long long)g64, d, kWave);
   }
   const int wave = threadIdx.x >> 6;
   if (lane_id() == 0) {
-    part[0][wave] = changed;
-    part[1][wave] = bad;
+    part[0][wave] = c64;
+    part[1][wave] = g64;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t c = part[0][0] + part[0][1] + part[0][2] + part[0][3];
-    const uint32_t g = part[1][0] + part[1][1] + part[1][2] + part[1][3];
-    if (c) atomicAdd(&stats[0], (unsigned long long)c);
-    if (g) atomicAdd(&stats[1], (unsigned long long)g);
+    unsigned long long c = 0, g = 0;
+#pragma unroll
+    for (int w = 0; w < kStatsThreads / kWave; ++w) {
+      c += part[0][w];
+      g += part[1][w];
+    }
+    if (c) atomicAdd(&stats[0], c);
+    if (g) atomicAdd(&stats[1], g);
   }
 }
 
@@ -521,13 +549,14 @@ hipError_t launch_mask_stats(const uint8_t* old_bits, const uint8_t* new_bits, i
   unsigned long long* st = reinterpret_cast<unsigned long long*>(stats);
   hipLaunchKernelGGL(zero_stats_kernel, dim3(1), dim3(64), 0, stream, st);
   const int64_t words = rows * cols / 32;
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((words / 4 + 255) / 256, 2048));
+  const int64_t blocks =
+      std::max<int64_t>(1, std::min<int64_t>((words / 16 + kStatsThreads - 1) / kStatsThreads, 256));
   const uint32_t* ow = reinterpret_cast<const uint32_t*>(old_bits);
   const uint32_t* nw = reinterpret_cast<const uint32_t*>(new_bits);
   if (m == 4)
-    hipLaunchKernelGGL(mask_stats_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, ow, nw, words, n, st);
+    hipLaunchKernelGGL(mask_stats_kernel<4>, dim3((unsigned)blocks), dim3(kStatsThreads), 0, stream, ow, nw, words, n, st);
   else
-    hipLaunchKernelGGL(mask_stats_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, ow, nw, words, n, st);
+    hipLaunchKernelGGL(mask_stats_kernel<8>, dim3((unsigned)blocks), dim3(kStatsThreads), 0, stream, ow, nw, words, n, st);
   return hipGetLastError();
 }
 
