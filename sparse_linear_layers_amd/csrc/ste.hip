@@ -296,7 +296,12 @@ __global__ __launch_bounds__(ste::NT, 2) void ste_kernel(SteArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < M && n < K) out[m * K + n] = acc[i][j][r];
+        if (m < M && n < K) {
+          // dx is final and written once: stream it past the caches; dw
+          // partials are read back by the reduction right after
+          if constexpr (DW) out[m * K + n] = acc[i][j][r];
+          else __builtin_nontemporal_store(acc[i][j][r], &out[m * K + n]);
+        }
       }
     }
 }
