@@ -70,6 +70,15 @@ struct RowJob {
   const float* scale_in;  // non-null: the row's scale is given (per-tensor gamma)
 };
 
+// 16 bytes of latent weights read with the non-temporal policy: a refresh
+// reads W once, and streaming it measured faster than cached loads (also
+// for a layer's matrices that fit in the Infinity Cache).
+__device__ __forceinline__ float4 load_w4_stream(const float4* p, int64_t idx) {
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p) + idx);
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+
 template <int CPL, int MODE>
 __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, int n,
                                                bool from_masked) {
@@ -82,7 +91,7 @@ __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, i
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int64_t idx = lane + (int64_t)kWave * c;
-    v[c] = idx < nchunks ? src[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[c] = idx < nchunks ? load_w4_stream(src, idx) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // ---- mask ----
 #pragma unroll
@@ -217,7 +226,7 @@ __device__ void quant_pack_row_long(const RowJob& job, int64_t row, int n, bool 
   uint32_t* dst = reinterpret_cast<uint32_t*>(job.packed + row * (cols >> 2));
   for (int64_t base = 0; base < nchunks; base += kWave) {
     const int64_t idx = base + lane;
-    float4 x = idx < nchunks ? src[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 x = idx < nchunks ? load_w4_stream(src, idx) : make_float4(0.f, 0.f, 0.f, 0.f);  // last read
     uint32_t k = mask_of(idx, x);
     const float w[4] = {x.x, x.y, x.z, x.w};
     uint32_t byte = 0;
