@@ -399,6 +399,12 @@ __device__ __forceinline__ uint32_t groups_not_n(uint32_t w, uint32_t n) {
   return (uint32_t)__popc(x);
 }
 
+// Mask words are read once: non-temporal loads.
+__device__ __forceinline__ uint4 load_u4_stream(const uint4* p, int64_t idx) {
+  const v4i t = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p) + idx);
+  return make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
+}
+
 // One block of 1024 threads per CU at most: few blocks keep the two 64-bit
 // atomics per block cheap (they serialise on one address), and four 16-byte
 // loads per operand and lane keep enough bytes in flight.
@@ -425,9 +431,9 @@ __global__ __launch_bounds__(kStatsThreads) void mask_stats_kernel(const uint32_
   for (; i + 3 * gsz < nvec; i += 4 * gsz) {
     uint4 a[4], b[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a[u] = nv[i + u * gsz];
+    for (int u = 0; u < 4; ++u) a[u] = load_u4_stream(nv, i + u * gsz);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) b[u] = old_w ? ov[i + u * gsz] : a[u];
+    for (int u = 0; u < 4; ++u) b[u] = old_w ? load_u4_stream(ov, i + u * gsz) : a[u];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       word(a[u].x, b[u].x);
