@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void gemv_kernel(GemvArgs a, i
   int un = u + (int)gridDim.x;
   GemvUnit dn = un < units ? fetch(un) : dc;  // read while this unit computes
   for (;;) {
-    const int K = dc.K, N = dc.N;
+    const int N = dc.N;
     const int64_t row0 = dc.row0;
 
     // Row scales of this lane's four rows per finished row group (rows past
