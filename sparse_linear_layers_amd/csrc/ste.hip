@@ -320,15 +320,33 @@ __global__ __launch_bounds__(256) void ste_dw_reduce_kernel(const float* __restr
   }
 }
 
-// Split of the token reduction of dw: enough blocks to cover the CUs twice,
-// chunks of at least 512 tokens (a multiple of the 32-token step).
+// Blocks of the dw kernel resident at once on the current device.
+static int64_t ste_slots() {
+  static int64_t slots = 0;
+  if (slots == 0) {
+    int dev = 0, cus = 0, occ = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ste_kernel<1>, ste::NT, 0) != hipSuccess || occ <= 0)
+      occ = 2;
+    slots = (int64_t)cus * occ;
+  }
+  return slots;
+}
+
+// Split of the token reduction of dw: as many splits as fit the output
+// tiles into one round of resident blocks (a second, partial round would
+// leave most CUs idle for a whole block), at most 32, with chunks of at
+// least 512 tokens (a multiple of the 32-token step).
 static int ste_splits(int64_t T, int64_t K, int64_t N, int64_t* chunk) {
   if (T <= 0) {  // empty reduction: one pass that writes zeros
     *chunk = ste::BR;
     return 1;
   }
   const int64_t tiles = ((N + ste::BM - 1) / ste::BM) * ((K + ste::BN - 1) / ste::BN);
-  int64_t S = std::max<int64_t>(1, std::min<int64_t>((512 + tiles - 1) / tiles, 32));
+  const int64_t slots = ste_slots();
+  int64_t S = tiles >= slots ? 1 : std::min<int64_t>(slots / tiles, 32);
   S = std::max<int64_t>(1, std::min<int64_t>(S, (T + 511) / 512));
   int64_t c = (T + S - 1) / S;
   c = (c + ste::BR - 1) / ste::BR * ste::BR;
