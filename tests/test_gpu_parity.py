@@ -321,6 +321,32 @@ def test_sparse24_matches_dense(sbl, T, K, N):
     assert_y_close(host(y), oracle.dequant(acc_ref, o["beta"], o["g"]))
 
 
+@pytest.mark.parametrize("name,N,K", [("q", 896, 896), ("gate", 4864, 896), ("down", 896, 4864)])
+def test_sparse24_full_size_sampled(sbl, name, N, K):
+    """The 2:4 product at the 0.5B skeleton's prefill size (32768 tokens), as
+    the benchmark runs it: acc and y on 96 sampled tokens against the
+    oracle, and y equal to the dense product's everywhere."""
+    T = synth.QWEN05B_PREFILL_TOKENS
+    W = synth.latent_weight(f"gpu/sp24full/{name}/W", N, K)
+    x = synth.activations_bf16(f"gpu/sp24full/{name}/x", T, K)
+    mask = oracle.nm_mask(W, 2, 4)
+    g, _ = oracle.row_scale(W)
+    codes = oracle.ternary_codes(W, mask, g)
+    xq, beta = oracle.act_quant(x)
+    packed = dev(oracle.pack_codes(codes))
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sp = sbl.sparse24_compress(packed, bad)
+    y, acc = sbl.sparse_bitlinear_gemm_sparse24(dev(xq), dev(beta), sp, N, dev(g), want_acc=True)
+    yd = sbl.sparse_bitlinear_gemm(dev(xq), dev(beta), packed, dev(g))[0]
+    assert int(bad.item()) == 0
+    assert torch.equal(y, yd)
+    rows = np.sort(synth.rng(f"gpu/sp24full/{name}/sample").choice(T, 96, replace=False))
+    rows[-1] = T - 1
+    acc_ref = oracle.gemm_acc(xq[rows], codes)
+    assert np.array_equal(host(acc)[rows], acc_ref)
+    assert_y_close(host(y)[rows], oracle.dequant(acc_ref, beta[rows], g))
+
+
 def test_sparse24_counts_groups_that_are_not_2of4(sbl):
     o = _operands("gpu/sp24/bad", 16, 256, 64, n=3, m=4)
     nz = (o["codes"].reshape(64, -1, 4) != 0).sum(-1)
@@ -358,6 +384,34 @@ def test_gemv_grouped(sbl, T):
         g = o["g"] if name == "v" else oracle.bf16_bits_to_float(o["gb"])
         acc_ref = oracle.gemm_acc(o["xq"], o["codes"])
         assert_y_close(host(j["y"]), oracle.dequant(acc_ref, o["beta"], g))
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_gemv_grouped_full_sweep(sbl, T):
+    """The decode sweep as the benchmark launches it: all 168 linears of the
+    0.5B skeleton (24 layers x 7) in one grouped call, bf16 row scales, one
+    x~ per input width; every output against the oracle."""
+    K_in = {"q": 896, "k": 896, "v": 896, "o": 896, "gate": 896, "up": 896, "down": 4864}
+    xs = {}
+    for K in (896, 4864):
+        x = synth.activations_bf16(f"gpu/gemvsweep/x/{K}/{T}", T, K)
+        xs[K] = oracle.act_quant(x)
+    xd = {K: (dev(v[0]), dev(v[1])) for K, v in xs.items()}
+    jobs, refs = [], []
+    for layer in range(synth.QWEN05B_LAYERS):
+        for name, N, K in synth.QWEN05B_LINEARS:
+            W = synth.latent_weight(f"gpu/gemvsweep/L{layer}/{name}", N, K)
+            g, gb = oracle.row_scale(W)
+            codes = oracle.ternary_codes(W, oracle.nm_mask(W, 3, 4), g)
+            jobs.append(dict(xq=xd[K][0], beta=xd[K][1], packed=dev(oracle.pack_codes(codes)),
+                             scale=dev(gb), y=torch.full((T, N), float("nan"), device=DEV)))
+            refs.append((codes, oracle.bf16_bits_to_float(gb), K))
+    hostd, devd = sbl.gemv_descs(jobs)
+    sbl.sparse_bitlinear_gemv_grouped(hostd, devd, len(jobs), T, DEV)
+    torch.cuda.synchronize()
+    for j, (codes, g, K) in zip(jobs, refs):
+        xq, beta = xs[K]
+        assert_y_close(host(j["y"]), oracle.dequant(oracle.gemm_acc(xq, codes), beta, g))
 
 
 # ------------------------------------------------------------- plumbing
