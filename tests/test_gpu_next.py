@@ -230,15 +230,16 @@ def test_ste_backward_empty_reductions(sbl):
     assert (host(got[0]) == 0).all() and got[1].shape == (0, K)
 
 
-def test_ste_backward_full_size_sampled(sbl):
-    """The 0.5B skeleton's gate linear at 32768 tokens: dx on sampled token
-    rows, dw on sampled input columns (each depends only on its own
-    slice), against the oracle."""
-    T, K, N = synth.QWEN05B_PREFILL_TOKENS, 896, 4864
-    o = _ste_operands("gpu/ste/full/gate", T, K, N)
+@pytest.mark.parametrize("name,N,K", [("gate", 4864, 896), ("down", 896, 4864)])
+def test_ste_backward_full_size_sampled(sbl, name, N, K):
+    """The 0.5B skeleton's gate and down linears at 32768 tokens: dx on
+    sampled token rows, dw on sampled input columns (each depends only on
+    its own slice), against the oracle."""
+    T = synth.QWEN05B_PREFILL_TOKENS
+    o = _ste_operands(f"gpu/ste/full/{name}", T, K, N)
     dx, dw = sbl.sparse_bitlinear_ste_backward(dev(o["dy"]), dev(o["xq"]), dev(o["beta"]),
                                                dev(o["packed"]), dev(o["g"]))
-    pick = synth.rng("gpu/ste/full/pick")
+    pick = synth.rng(f"gpu/ste/full/pick/{name}")
     rows = np.unique(np.concatenate([[0, T - 1], pick.choice(T, 62, replace=False)]))
     cols = np.unique(np.concatenate([[0, K - 1], pick.choice(K, 30, replace=False)]))
     dx_ref, _ = oracle.ste_backward(o["dy"][rows], o["xq"][rows], o["beta"][rows], o["codes"],
