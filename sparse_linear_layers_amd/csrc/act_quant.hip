@@ -12,22 +12,16 @@
 
 namespace sbl {
 
-// 16 bytes of x; STREAM: a non-temporal load (x larger than half the
-// 256 MB Infinity Cache is read once and would only evict other data; a
-// smaller x is usually still cached from its producer, and a streaming load
-// would give that up)
-template <bool STREAM>
+// 16 bytes of x on their last read, with the non-temporal policy: x is read
+// once and would only evict the weights and x~ that the products read next
+// (a layer step with streaming activation loads ran ~5% faster, although a
+// lone quantisation of an x that is still cached is a little slower).
 __device__ __forceinline__ uint4 load_x16(const uint4* p, int64_t idx) {
-  if constexpr (STREAM) {
-    const v4i t = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p) + idx);
-    return make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
-  } else {
-    return p[idx];
-  }
+  const v4i t = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p) + idx);
+  return make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
 }
-constexpr int64_t kStreamBytes = int64_t(128) << 20;
 
-template <int CPL, bool STREAM>  // 8-element (16-byte) chunks per lane; 0 = long-row loop
+template <int CPL>  // 8-element (16-byte) chunks per lane; 0 = long-row loop
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x,
                                                         int64_t tokens, int64_t cols,
                                                         int8_t* __restrict__ xq,
@@ -66,7 +60,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int64_t idx = lane + (int64_t)kWave * c;
-      v[c] = idx < nchunks ? load_x16<STREAM>(src, idx) : make_uint4(0u, 0u, 0u, 0u);
+      v[c] = idx < nchunks ? load_x16(src, idx) : make_uint4(0u, 0u, 0u, 0u);
       m = chunk_max(v[c], m);
     }
     m = wave_max(m);
@@ -88,7 +82,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
     const float s = __fdiv_rn(127.0f, b);
     for (int64_t base = 0; base < nchunks; base += kWave) {
       const int64_t idx = base + lane;
-      if (idx < nchunks) dst[idx] = quant8(load_x16<STREAM>(src, idx), s);  // second, last read
+      if (idx < nchunks) dst[idx] = quant8(load_x16(src, idx), s);  // second, last read
     }
     if (lane == 0) beta[t] = b;
   }
@@ -106,7 +100,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
 // then beta, s and x~ exactly as act_quant_kernel does on n.  The weight
 // (4 B per channel) is shared by every token and stays in L2.
 // ---------------------------------------------------------------------------
-template <int CPL, bool STREAM>  // 8-element chunks per lane; 0 = long rows (three passes)
+template <int CPL>  // 8-element chunks per lane; 0 = long rows (three passes)
 __global__ __launch_bounds__(256) void rmsnorm_act_quant_kernel(const uint16_t* __restrict__ x,
                                                                 const float* __restrict__ w,
                                                                 float eps, int64_t tokens,
@@ -170,7 +164,7 @@ __global__ __launch_bounds__(256) void rmsnorm_act_quant_kernel(const uint16_t* 
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int64_t idx = lane + (int64_t)kWave * c;
-      v[c] = idx < nchunks ? load_x16<STREAM>(src, idx) : make_uint4(0u, 0u, 0u, 0u);
+      v[c] = idx < nchunks ? load_x16(src, idx) : make_uint4(0u, 0u, 0u, 0u);
       ss = chunk_ss(v[c], ss);
     }
     const float r = inv_rms(wave_sum(ss));
@@ -216,7 +210,7 @@ __global__ __launch_bounds__(256) void rmsnorm_act_quant_kernel(const uint16_t* 
       const int64_t idx = base + lane;
       if (idx < nchunks) {
         float n[8];
-        normalise(load_x16<STREAM>(src, idx), idx, r, n);  // third, last read
+        normalise(load_x16(src, idx), idx, r, n);  // third, last read
         dst[idx] = quant8(n, s);
       }
     }
@@ -228,14 +222,8 @@ hipError_t launch_rmsnorm_act_quant(const uint16_t* x, const float* w, float eps
                                     int64_t cols, int8_t* xq, float* beta, hipStream_t stream) {
   const int64_t need = (cols / 8 + kWave - 1) / kWave;
   const dim3 grid((unsigned)((tokens + 3) / 4)), block(256);
-  const bool stream_x = tokens * cols * 2 > kStreamBytes;
-#define SBL_RQ(C)                                                                                   \
-  do {                                                                                              \
-    if (stream_x)                                                                                   \
-      hipLaunchKernelGGL((rmsnorm_act_quant_kernel<C, true>), grid, block, 0, stream, x, w, eps, tokens, cols, xq, beta);  \
-    else                                                                                            \
-      hipLaunchKernelGGL((rmsnorm_act_quant_kernel<C, false>), grid, block, 0, stream, x, w, eps, tokens, cols, xq, beta); \
-  } while (0)
+#define SBL_RQ(C) \
+  hipLaunchKernelGGL(rmsnorm_act_quant_kernel<C>, grid, block, 0, stream, x, w, eps, tokens, cols, xq, beta)
   if (need <= 1) SBL_RQ(1);
   else if (need <= 2) SBL_RQ(2);
   else if (need <= 4) SBL_RQ(4);
@@ -252,14 +240,7 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t tokens, int64_t cols, int
                             float* beta, hipStream_t stream) {
   const int64_t need = (cols / 8 + kWave - 1) / kWave;
   const dim3 grid((unsigned)((tokens + 3) / 4)), block(256);
-  const bool stream_x = tokens * cols * 2 > kStreamBytes;
-#define SBL_AQ(C)                                                                                  \
-  do {                                                                                             \
-    if (stream_x)                                                                                  \
-      hipLaunchKernelGGL((act_quant_kernel<C, true>), grid, block, 0, stream, x, tokens, cols, xq, beta);  \
-    else                                                                                           \
-      hipLaunchKernelGGL((act_quant_kernel<C, false>), grid, block, 0, stream, x, tokens, cols, xq, beta); \
-  } while (0)
+#define SBL_AQ(C) hipLaunchKernelGGL(act_quant_kernel<C>, grid, block, 0, stream, x, tokens, cols, xq, beta)
   if (need <= 1) SBL_AQ(1);
   else if (need <= 2) SBL_AQ(2);
   else if (need <= 4) SBL_AQ(4);
