@@ -19,6 +19,8 @@
 // group gq with B lane group gq/4 bytes 16*G + 4*(gq%4) + index, and B lane
 // group h is given x~ columns 32*h .. 32*h + 31 of the block: every kept
 // weight meets its own activation.
+#include <type_traits>
+
 #include "sbl_device.h"
 #include "sbl_launch.h"
 
@@ -85,10 +87,11 @@ hipError_t launch_sparse24_compress(const uint8_t* packed, int64_t N, int64_t K,
 }
 
 // ---------------------------------------------------------------------------
-// smfmac GEMM: the structure of the dense product kernel (persistent blocks
-// over XCD-contiguous tile ranges, flattened (tile, k-step) loop, two
-// register stages, double-buffered LDS), one 64-wide k step per stage and
-// one smfmac per 32x32 tile pair per step.
+// smfmac GEMM for problems with fewer 256 x 256 tiles than CUs (or N % 4 !=
+// 0): the structure of the dense small-tile kernel (persistent blocks over
+// XCD-contiguous tile ranges, flattened (tile, k-step) loop, two register
+// stages, double-buffered LDS), one 64-wide k step per stage and one smfmac
+// per 32x32 tile pair per step.
 // ---------------------------------------------------------------------------
 struct Sp24Args {
   const int8_t* xq;
@@ -292,6 +295,274 @@ __global__ __launch_bounds__(256, 2) void gemm_sp24_kernel(Sp24Args a) {
 #undef SBL_STORE
 }
 
+// ---------------------------------------------------------------------------
+// Warp-specialised smfmac kernel for problems with at least one 256 x 256
+// tile per CU: the structure of the dense warp-specialised product (one
+// persistent 768-thread block per CU, 8 math and 4 loader waves, 128-wide
+// k steps two ahead in registers, double-buffered LDS, XCD-contiguous tile
+// ranges), with the weights as the sparse A operand.
+//  * Math wave w holds 128 (o) x 64 (t) int32 accumulators (waves 2 (o) x
+//    4 (t) over the tile) and runs two smfmac blocks of 64 k per step.
+//  * Per step and weight row a loader thread reads the 32 image bytes of
+//    the two blocks, expands the four 16-value halves to int8, stored as
+//    [block][row][half] with the halves swapped on rows with bit 3 set (so
+//    the 16-byte fragment reads of 16 consecutive rows hit every bank once),
+//    and stores the four index words as [block][row][half], so one 32-bit
+//    read per lane covers 64 banks.  Every fragment address is then one
+//    per-lane base plus a constant.
+//  * Epilogue: the A-operand layout gives lane l token l%32 and four
+//    consecutive features per register group, so each 32 x 32 block passes
+//    through a per-wave LDS patch (row = token) and returns as 16-byte
+//    pieces, eight lanes per 128-byte row of y: every store writes whole
+//    lines.
+namespace spws {
+constexpr int BO = 256, BT = 256, BK = 128, NT = 768;
+constexpr int MATH = 8;
+constexpr int XS = BK + 16;  // bytes per staged x~ row
+constexpr int VS = 32;       // bytes per staged weight row and block: 2 halves of 16 kept values
+constexpr int WO = 128, WT = 64;
+constexpr int TO = WO / 32, TT = WT / 32;
+constexpr int XQ = BT / 32;
+constexpr int ES = 144;  // bytes per row of the epilogue patch (padded: 16 rows x 16 B hit all banks)
+}  // namespace spws
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sp_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)min(bytes, (int64_t)INT32_MAX), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 sp_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+// y is written once and never read back: its stores carry the non-temporal
+// policy (bit 1 of the policy operand).
+constexpr int kSpStoreNonTemporal = 2;
+
+template <bool SCALE_BF16>
+__global__ __launch_bounds__(spws::NT, 1) void gemm_sp24_ws_kernel(Sp24Args a) {
+  using namespace spws;
+  __shared__ __attribute__((aligned(16))) int8_t sX[2][BT * XS];       // x~ rows (tokens)
+  __shared__ __attribute__((aligned(16))) int8_t sV[2][2][BO * VS];    // expanded kept values
+  __shared__ __attribute__((aligned(16))) uint32_t sI[2][2][BO * 2];   // index words
+  __shared__ __attribute__((aligned(16))) float sG[2][BO];             // row scales, by tile parity
+  __shared__ __attribute__((aligned(16))) float sBt[2][BT];            // beta/127, by tile parity
+  __shared__ __attribute__((aligned(16))) int8_t sE[MATH][32 * ES];          // epilogue patches
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t K = a.K, N = a.N, T = a.T;
+  const int rowbytes = (int)(K >> 2);
+  const int KB = (int)(K >> 6);  // 64-wide smfmac blocks
+  const int KT = (KB + 1) >> 1;  // 128-wide steps
+
+  const SpTileRange tr = sp_tile_range(blockIdx.x, gridDim.x, a.ntiles);
+  if (tr.first >= tr.end) return;
+  const int total = ((tr.end - tr.first + tr.step - 1) / tr.step) * KT;
+  const int total2 = (total + 1) & ~1;  // both roles pass the same (even) number of barriers
+
+  if (wave < MATH) {
+    // ------------------------------ math waves ------------------------------
+    const int wo = wave & 1, wt = wave >> 1;
+    const int G = lane >> 5, l32 = lane & 31;
+    v16i acc[TO][TT];
+#pragma unroll
+    for (int i = 0; i < TO; ++i)
+#pragma unroll
+      for (int j = 0; j < TT; ++j) acc[i][j] = v16i{};
+
+    auto epilogue = [&](int tile, int par) {
+      const int64_t o0 = (int64_t)(tile % a.tiles_o) * BO;
+      const int64_t t0 = (int64_t)(tile / a.tiles_o) * BT;
+      const int64_t rows_t = min((int64_t)BT, T - t0);
+      const int N4 = (int)N * 4;
+      const __amdgpu_buffer_rsrc_t ry = sp_rsrc(a.y + t0 * N, rows_t * N * 4);
+      const __amdgpu_buffer_rsrc_t ra =
+          sp_rsrc(a.acc ? static_cast<const void*>(a.acc + t0 * N) : a.y, a.acc ? rows_t * N * 4 : 0);
+      int8_t* const e = sE[wave];
+      const int rr = lane >> 3, cc = lane & 7;  // read-back: rows rr + 8v, 16-byte unit cc
+#pragma unroll
+      for (int i = 0; i < TO; ++i) {
+        const int ol = wo * WO + i * 32 + 4 * cc;
+        const float4 g = *reinterpret_cast<const float4*>(&sG[par][ol]);
+        const uint32_t vo = o0 + ol < N ? (uint32_t)((o0 + ol) * 4) : 0x80000000u;  // past N: dropped
+#pragma unroll
+        for (int j = 0; j < TT; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            *reinterpret_cast<v4i*>(e + l32 * ES + 16 * (2 * q + G)) =
+                v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r = 8 * v + rr;
+            const v4i c = *reinterpret_cast<const v4i*>(e + r * ES + 16 * cc);
+            const int tl = wt * WT + j * 32 + r;
+            const float bt = sBt[par][tl];
+            const uint32_t off = vo + (uint32_t)(tl * N4);
+            const v4i yv = v4i{(int)__float_as_uint(((float)c.x * bt) * g.x),
+                               (int)__float_as_uint(((float)c.y * bt) * g.y),
+                               (int)__float_as_uint(((float)c.z * bt) * g.z),
+                               (int)__float_as_uint(((float)c.w * bt) * g.w)};
+            __builtin_amdgcn_raw_buffer_store_b128(yv, ry, (int)off, 0, kSpStoreNonTemporal);
+            if (a.acc) __builtin_amdgcn_raw_buffer_store_b128(c, ra, (int)off, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TO; ++i)
+#pragma unroll
+        for (int j = 0; j < TT; ++j) acc[i][j] = v16i{};
+    };
+
+    // per-lane fragment bases: weight row wo*WO + l32 (+32 i), half G
+    // (swapped on rows with bit 3 set); token row wt*WT + l32 (+32 j)
+    const int a_off = (wo * WO + l32) * VS + 16 * (G ^ ((l32 >> 3) & 1));
+    const int i_off = 2 * (wo * WO + l32) + G;
+    const int x_off = (wt * WT + l32) * XS + 32 * G;
+    auto mma = [&](auto bufc) {
+      constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // the token fragments stay in registers, the weight fragments
+        // stream through one 32-row block at a time
+        v8i bf[TT];
+#pragma unroll
+        for (int j = 0; j < TT; ++j) {
+          const int8_t* p = sX[buf] + x_off + j * 32 * XS + 64 * kb;
+          const v4i lo = *reinterpret_cast<const v4i*>(p);
+          const v4i hi = *reinterpret_cast<const v4i*>(p + 16);
+          bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int i = 0; i < TO; ++i) {
+          const v4i af = *reinterpret_cast<const v4i*>(sV[buf][kb] + a_off + i * 32 * VS);
+          const int ix = (int)sI[buf][kb][i_off + 64 * i];
+#pragma unroll
+          for (int j = 0; j < TT; ++j)
+            acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(af, bf[j], acc[i][j], ix, 0, 0);
+        }
+      }
+    };
+
+    int tile = tr.first, kt = 0, par = 0;
+    auto advance = [&]() {
+      if (++kt == KT) {
+        epilogue(tile, par);
+        kt = 0;
+        tile += tr.step;
+        par ^= 1;
+      }
+    };
+    __syncthreads();  // step 0 staged
+    for (int s = 0; s < total2; s += 2) {
+      if (s < total) {
+        mma(std::integral_constant<int, 0>{});
+        advance();
+      }
+      __syncthreads();
+      if (s + 1 < total) {
+        mma(std::integral_constant<int, 1>{});
+        advance();
+      }
+      __syncthreads();
+    }
+  } else {
+    // ----------------------------- loader waves -----------------------------
+    // Thread lt stages image row lt (32 bytes per step) and x~ rows
+    // x_row + 32 q (q < 8), bytes x_part..+16 of the step's 128.  The values
+    // of a block past K (K % 128 == 64) are zeroed when staged, which makes
+    // whatever x~ and index bits sit there irrelevant.
+    const int lt = tid - MATH * 64;
+    const int x_row = lt >> 3, x_part = (lt & 7) * 16;
+    const int c_vbase = lt * rowbytes;
+    const int x_vbase = x_row * (int)K + x_part;
+    const int x_q = 32 * (int)K;
+    const int sw = (lt >> 3) & 1;
+    int8_t* const vdst = &sV[0][0][lt * VS];
+    int8_t* const xdst = &sX[0][x_row * XS + x_part];
+
+    int ld_tile = tr.first, ld_kt = 0, ld_par = 0;
+    int64_t ld_o0 = 0, ld_t0 = 0;
+    __amdgpu_buffer_rsrc_t rc, rx;
+    auto rebase = [&]() {
+      ld_o0 = (int64_t)(ld_tile % a.tiles_o) * BO;
+      ld_t0 = (int64_t)(ld_tile / a.tiles_o) * BT;
+      rc = sp_rsrc(a.sp + ld_o0 * rowbytes, min((int64_t)BO, N - ld_o0) * rowbytes);
+      rx = sp_rsrc(a.xq + ld_t0 * K, min((int64_t)BT, T - ld_t0) * K);
+    };
+    rebase();
+
+    uint4 c0, c1, d0, d1, x0[XQ], x1[XQ];
+    uint32_t g0, g1, b0, b1;
+    int kt0, kt1, par0, par1;
+#define SBL_LOAD(S)                                                                     \
+  {                                                                                     \
+    kt##S = ld_kt;                                                                      \
+    par##S = ld_par;                                                                    \
+    c##S = sp_load16(rc, c_vbase + 32 * ld_kt);                                         \
+    d##S = sp_load16(rc, c_vbase + 32 * ld_kt + 16);                                    \
+    _Pragma("unroll") for (int q = 0; q < XQ; ++q) x##S[q] = sp_load16(rx, x_vbase + q * x_q + BK * ld_kt); \
+    const int64_t so_ = min(ld_o0 + lt, N - 1);                                         \
+    g##S = SCALE_BF16 ? (uint32_t)reinterpret_cast<const uint16_t*>(a.scale)[so_] << 16 \
+                      : reinterpret_cast<const uint32_t*>(a.scale)[so_];                \
+    b##S = reinterpret_cast<const uint32_t*>(a.beta)[min(ld_t0 + lt, T - 1)];           \
+    if (++ld_kt == KT) {                                                                \
+      if (ld_tile + tr.step < tr.end) {                                                 \
+        ld_kt = 0;                                                                      \
+        ld_tile += tr.step;                                                             \
+        ld_par ^= 1;                                                                    \
+        rebase();                                                                       \
+      } else {                                                                          \
+        ld_kt = KT - 1;                                                                 \
+      }                                                                                 \
+    }                                                                                   \
+  }
+#define SBL_WRITE(S, buf)                                                               \
+  {                                                                                     \
+    int8_t* v_ = vdst + (buf) * (2 * BO * VS);                                          \
+    const bool ka_ = 2 * kt##S < KB, kb_ = 2 * kt##S + 1 < KB;                          \
+    uint32_t e_[4];                                                                     \
+    expand16_strided(ka_ ? c##S.x : 0u, e_);                                            \
+    *reinterpret_cast<uint4*>(v_ + 16 * sw) = make_uint4(e_[0], e_[1], e_[2], e_[3]);   \
+    expand16_strided(ka_ ? c##S.z : 0u, e_);                                            \
+    *reinterpret_cast<uint4*>(v_ + 16 * (1 - sw)) = make_uint4(e_[0], e_[1], e_[2], e_[3]); \
+    expand16_strided(kb_ ? d##S.x : 0u, e_);                                            \
+    *reinterpret_cast<uint4*>(v_ + BO * VS + 16 * sw) = make_uint4(e_[0], e_[1], e_[2], e_[3]); \
+    expand16_strided(kb_ ? d##S.z : 0u, e_);                                            \
+    *reinterpret_cast<uint4*>(v_ + BO * VS + 16 * (1 - sw)) = make_uint4(e_[0], e_[1], e_[2], e_[3]); \
+    *reinterpret_cast<uint2*>(&sI[buf][0][2 * lt]) = make_uint2(c##S.y, c##S.w);       \
+    *reinterpret_cast<uint2*>(&sI[buf][1][2 * lt]) = make_uint2(d##S.y, d##S.w);       \
+    _Pragma("unroll") for (int q = 0; q < XQ; ++q)                                      \
+      *reinterpret_cast<uint4*>(xdst + (buf) * (BT * XS) + q * 32 * XS) = x##S[q];      \
+    if (kt##S == 0) {                                                                   \
+      sBt[par##S][lt] = __fdiv_rn(__uint_as_float(b##S), 127.0f);                       \
+      sG[par##S][lt] = __uint_as_float(g##S);                                           \
+    }                                                                                   \
+  }
+
+    SBL_LOAD(0);
+    SBL_WRITE(0, 0);
+    SBL_LOAD(1);
+    SBL_LOAD(0);
+    __syncthreads();
+    for (int s = 0; s < total2; s += 2) {
+      if (s + 1 < total) SBL_WRITE(1, 1);  // step s+1
+      SBL_LOAD(1);                         // step s+3
+      __asm__ volatile("" ::: "memory");
+      __syncthreads();
+      if (s + 2 < total) SBL_WRITE(0, 0);  // step s+2
+      SBL_LOAD(0);                         // step s+4
+      __asm__ volatile("" ::: "memory");
+      __syncthreads();
+    }
+#undef SBL_LOAD
+#undef SBL_WRITE
+  }
+}
+
 static int sp_num_cus() {
   static int n = 0;
   if (n == 0) {
@@ -311,6 +582,20 @@ hipError_t launch_gemm_sparse24(const int8_t* xq, const float* beta, const void*
   constexpr int BM = 128, BN = 128;
   Sp24Args a{xq, beta, reinterpret_cast<const uint8_t*>(sp), scale, y, acc, T, K, N, scale_bf16,
              (N % 4) == 0, 0, 0};
+  const int64_t ws_o = (N + spws::BO - 1) / spws::BO, ws_t = (T + spws::BT - 1) / spws::BT;
+  if (ws_o * ws_t > INT32_MAX) return hipErrorInvalidValue;
+  // the warp-specialised kernel stores whole 16-byte pieces (N % 4 == 0) and
+  // keeps 32-bit buffer offsets within a tile's rows of y
+  if (N % 4 == 0 && ws_o * ws_t >= sp_num_cus() && (int64_t)spws::BT * N * 4 < INT32_MAX / 2) {
+    a.tiles_o = (int)ws_o;
+    a.ntiles = (int)(ws_o * ws_t);
+    const int grid = (int)std::min<int64_t>(a.ntiles, sp_num_cus());
+    if (scale_bf16)
+      hipLaunchKernelGGL(gemm_sp24_ws_kernel<true>, dim3((unsigned)grid), dim3(spws::NT), 0, stream, a);
+    else
+      hipLaunchKernelGGL(gemm_sp24_ws_kernel<false>, dim3((unsigned)grid), dim3(spws::NT), 0, stream, a);
+    return hipGetLastError();
+  }
   a.tiles_o = (int)((N + BM - 1) / BM);
   a.ntiles = (int)((int64_t)a.tiles_o * ((T + BN - 1) / BN));
   int occ = 1;

@@ -347,6 +347,57 @@ def test_sparse24_full_size_sampled(sbl, name, N, K):
     assert_y_close(host(y)[rows], oracle.dequant(acc_ref, beta[rows], g))
 
 
+@pytest.mark.parametrize("T,K,N,bf16_scale", [(16400, 320, 1000, False), (16400, 192, 1004, True),
+                                                (8292, 896, 4864, False), (16385, 4864, 896, True),
+                                                (16400, 192, 1002, False)])
+def test_sparse24_large_tiles(sbl, T, K, N, bf16_scale):
+    """Sizes that take the large-tile smfmac kernel (at least one 256 x 256
+    tile per CU, N % 4 == 0): ragged token and row edges, K % 128 == 64,
+    bf16 row scales; N % 4 != 0 takes the small-tile kernel.  y equal to the
+    dense product's everywhere; acc and y against the oracle on token rows
+    that cover whole tiles at both ends."""
+    o = _operands(f"gpu/sp24_big/{T}x{K}x{N}", T, K, N, n=2, m=4)
+    scale = dev(o["gb"]) if bf16_scale else dev(o["g"])
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sp = sbl.sparse24_compress(dev(o["packed"]), bad)
+    y, acc = sbl.sparse_bitlinear_gemm_sparse24(dev(o["xq"]), dev(o["beta"]), sp, N, scale,
+                                                want_acc=True)
+    yd = sbl.sparse_bitlinear_gemm(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), scale)[0]
+    assert int(bad.item()) == 0
+    assert torch.equal(y, yd)
+    rnd = synth.rng(f"gpu/sp24_big/{T}x{K}x{N}/rows").choice(T, 64, replace=False)
+    rows = np.unique(np.concatenate([np.arange(300), np.arange(T - 300, T), rnd]))
+    acc_ref = oracle.gemm_acc(o["xq"][rows], o["codes"])
+    assert np.array_equal(host(acc)[rows], acc_ref)
+    g_used = oracle.bf16_bits_to_float(o["gb"]) if bf16_scale else o["g"]
+    assert_y_close(host(y)[rows], oracle.dequant(acc_ref, o["beta"][rows], g_used))
+
+
+def test_sparse24_stores_stay_in_bounds(sbl):
+    """y and the int32 hook of the large-tile smfmac kernel sit inside larger
+    buffers filled with a sentinel: rows past T and the columns past N of the
+    partial feature tile must never be written."""
+    T, K, N = 16400, 320, 1000
+    o = _operands(f"gpu/sp24_guard/{T}x{K}x{N}", T, K, N, n=2, m=4)
+    pad = 300
+    ybig = torch.full(((T + pad) * N + 64,), float("nan"), dtype=torch.float32, device=DEV)
+    abig = torch.full(((T + pad) * N + 64,), -7, dtype=torch.int32, device=DEV)
+    sp = sbl.sparse24_compress(dev(o["packed"]))
+    xq, beta, g = dev(o["xq"]), dev(o["beta"]), dev(o["g"])
+    y, acc = ybig[:T * N].view(T, N), abig[:T * N].view(T, N)
+    st = sbl.load().sparse_bitlinear_gemm_sparse24(
+        sbl._ptr(xq), sbl._ptr(beta), sbl._ptr(sp), sbl._ptr(g), sbl._scale_dtype(g), T, K, N,
+        sbl._ptr(y), sbl._ptr(acc), sbl._stream(xq.device))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert np.isnan(host(ybig[T * N:])).all(), "stores past the end of y"
+    assert (host(abig[T * N:]) == -7).all(), "stores past the end of acc"
+    rows = np.unique(np.concatenate([np.arange(260), np.arange(T - 260, T)]))
+    acc_ref = oracle.gemm_acc(o["xq"][rows], o["codes"])
+    assert np.array_equal(host(acc)[rows], acc_ref)
+    assert_y_close(host(y)[rows], oracle.dequant(acc_ref, o["beta"][rows], o["g"]))
+
+
 def test_sparse24_counts_groups_that_are_not_2of4(sbl):
     o = _operands("gpu/sp24/bad", 16, 256, 64, n=3, m=4)
     nz = (o["codes"].reshape(64, -1, 4) != 0).sum(-1)
