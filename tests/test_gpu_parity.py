@@ -303,6 +303,64 @@ def test_full_size_layer_sampled(sbl, name, N, K):
     assert_y_close(host(y_d)[rows], oracle.dequant(acc_ref, beta[rows], g))
 
 
+def test_full_size_fused_projection_step(sbl):
+    """The benchmark's layer step as it launches it: the 7 latent matrices of
+    the 0.5B skeleton refreshed in one grouped launch into the row ranges of
+    four projection buffers (q/k/v, o, gate/up, down), the 4 activation
+    inputs quantised, and 4 products at 32768 tokens.  Codes and scales of
+    every linear and x~ / beta compared in full against the oracle, acc and
+    y on 96 sampled tokens; the k and gate column slices equal the products
+    launched on their own."""
+    T = synth.QWEN05B_PREFILL_TOKENS
+    dims = {name: (N, K) for name, N, K in synth.QWEN05B_LINEARS}
+    groups = (("qkv", ("q", "k", "v"), "attn_in", 896), ("o", ("o",), "attn_out", 896),
+              ("gate_up", ("gate", "up"), "mlp_in", 896), ("down", ("down",), "mlp_hidden", 4864))
+    W = {name: synth.latent_weight(f"gpu/fused/{name}/W", N, K) for name, (N, K) in dims.items()}
+    packed_f, scale_f, packed, scale = {}, {}, {}, {}
+    for gname, members, _, K in groups:
+        N = sum(dims[mn][0] for mn in members)
+        packed_f[gname] = torch.empty((N, K // 4), dtype=torch.uint8, device=DEV)
+        scale_f[gname] = torch.empty(N, dtype=torch.float32, device=DEV)
+        r0 = 0
+        for mn in members:
+            packed[mn] = packed_f[gname][r0:r0 + dims[mn][0]]
+            scale[mn] = scale_f[gname][r0:r0 + dims[mn][0]]
+            r0 += dims[mn][0]
+    Wd = {name: dev(w) for name, w in W.items()}
+    jobs = [dict(W=Wd[name], packed=packed[name], scale=scale[name]) for name in dims]
+    h, d = sbl.refresh_descs(jobs)
+    sbl.nm_mask_quant_pack_grouped(h, d, len(jobs), 3, 4, 0, torch.device(DEV))
+    codes = {}
+    for name, w in W.items():
+        g, _ = oracle.row_scale(w)
+        codes[name] = oracle.ternary_codes(w, oracle.nm_mask(w, 3, 4), g)
+        assert np.array_equal(host(packed[name]), oracle.pack_codes(codes[name])), name
+        assert np.array_equal(host(scale[name]), g), name
+    rows = np.sort(synth.rng("gpu/fused/sample").choice(T, 96, replace=False))
+    rows[-1] = T - 1
+    rows_d = torch.from_numpy(rows).to(DEV)
+    ys = {}
+    for gname, members, xn, K in groups:
+        x = synth.activations_bf16(f"gpu/fused/{xn}/x", T, K)
+        xq_d, beta_d = sbl.act_quant_i8(dev(x))
+        xq, beta = oracle.act_quant(x)
+        assert np.array_equal(host(xq_d), xq), xn
+        assert np.array_equal(host(beta_d), beta), xn
+        y_d, acc_d = sbl.sparse_bitlinear_gemm(xq_d, beta_d, packed_f[gname], scale_f[gname],
+                                               want_acc=True)
+        c = np.concatenate([codes[mn] for mn in members])
+        g = host(scale_f[gname])
+        acc_ref = oracle.gemm_acc(xq[rows], c)
+        assert np.array_equal(host(acc_d[rows_d]), acc_ref), gname
+        assert_y_close(host(y_d[rows_d]), oracle.dequant(acc_ref, beta[rows], g))
+        for mn in members:
+            if mn in ("k", "gate"):
+                r0 = sum(dims[o][0] for o in members[:members.index(mn)])
+                alone = sbl.sparse_bitlinear_gemm(xq_d, beta_d, packed[mn], scale[mn])[0]
+                assert torch.equal(y_d[:, r0:r0 + dims[mn][0]], alone), mn
+        del y_d, acc_d
+
+
 # ------------------------------------------------------------------ 2:4
 @pytest.mark.parametrize("T,K,N", [(128, 256, 512), (300, 896, 200), (65, 4864, 896), (7, 64, 36)])
 def test_sparse24_matches_dense(sbl, T, K, N):
