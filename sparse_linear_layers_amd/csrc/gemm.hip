@@ -582,30 +582,17 @@ __global__ __launch_bounds__(ws::NT, 1) void gemm_i8_ws_kernel(GemmArgs a) {
   }
 }
 
-static int g_num_cus = 0;
-
-static int num_cus() {
-  if (g_num_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      g_num_cus = n;
-    else
-      g_num_cus = 256;
-  }
-  return g_num_cus;
-}
-
 template <int BM, int BN, int NSET>
 static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   a.tiles_o = (int)((a.N + BM - 1) / BM);
   const int64_t tiles_t = (a.T + BN - 1) / BN;
   a.ntiles = (int)((int64_t)a.tiles_o * tiles_t);
-  int occ = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_i8_kernel<BM, BN, NSET>, 256, 0) !=
-          hipSuccess || occ < 1)
-    occ = 1;
-  const int grid = (int)std::min<int64_t>(a.ntiles, (int64_t)occ * num_cus());
+  static std::atomic<int> occ_cache[kMaxDevices];
+  const int dev = stream_device(stream);
+  const int occ = per_device_cached(occ_cache, dev, [] {
+    return kernel_occupancy(reinterpret_cast<const void*>(gemm_i8_kernel<BM, BN, NSET>), 256, 1);
+  });
+  const int grid = (int)std::min<int64_t>(a.ntiles, (int64_t)occ * device_cus(dev));
   hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, NSET>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -615,7 +602,7 @@ hipError_t launch_gemm(const int8_t* xq, const float* beta, const uint8_t* packe
                        int32_t* acc, hipStream_t stream) {
   GemmArgs a{xq, beta, packed, scale, y, acc, T, K, N, scale_bf16, (N % 4) == 0, 0, 0};
   const int64_t ws_o = (N + ws::BO - 1) / ws::BO, ws_t = (T + ws::BT - 1) / ws::BT;
-  const int cus = num_cus();
+  const int cus = device_cus(stream_device(stream));
   if (ws_o * ws_t > INT32_MAX || ((N + 127) / 128) * ((T + 127) / 128) > INT32_MAX)
     return hipErrorInvalidValue;
   // the warp-specialised kernel keeps 32-bit buffer offsets within a tile's

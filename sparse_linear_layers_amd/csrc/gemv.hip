@@ -248,23 +248,15 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void gemv_kernel(GemvArgs a, i
   }
 }
 
-static int gemv_num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, c = 0;
-    n = (hipGetDevice(&dev) == hipSuccess &&
-         hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
-            ? c
-            : 256;
-  }
-  return n;
-}
-
-// Persistent blocks per CU: as many as the register file holds.
-static int gemv_resident_blocks() {
-  int occ = 0;
-  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_kernel<4>, 256, 0);
-  return (e == hipSuccess && occ > 0) ? occ : 2;
+// Persistent blocks of the decode kernel on the device of `stream`: as
+// many per CU as the register file holds.
+static int gemv_resident_slots(hipStream_t stream) {
+  static std::atomic<int> occ_cache[kMaxDevices];
+  const int dev = stream_device(stream);
+  const int occ = per_device_cached(occ_cache, dev, [] {
+    return kernel_occupancy(reinterpret_cast<const void*>(gemv_kernel<4>), 256, 2);
+  });
+  return occ * device_cus(dev);
 }
 
 // Row groups per block for a token count.
@@ -301,7 +293,7 @@ hipError_t launch_gemv(const sbl_gemv_desc* host, const sbl_gemv_desc* dev, int 
     }
     a.block_start[n] = (int)blocks;
     if (blocks > 0) {
-      const int grid = (int)std::min<int64_t>(blocks, (int64_t)gemv_resident_blocks() * gemv_num_cus());
+      const int grid = (int)std::min<int64_t>(blocks, (int64_t)gemv_resident_slots(stream));
       hipLaunchKernelGGL(gemv_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, a, (int)blocks);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

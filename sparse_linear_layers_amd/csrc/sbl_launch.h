@@ -7,10 +7,67 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "sbl.h"
 
 namespace sbl {
+
+// Per-device cache of a positive host query (CU count, occupancy): slot
+// `dev` holds the answer once asked; devices past the table are asked every
+// time.  Lock-free: concurrent first calls may both query and store the
+// same value.
+constexpr int kMaxDevices = 64;
+template <typename F>
+inline int per_device_cached(std::atomic<int> (&cache)[kMaxDevices], int dev, F&& query) {
+  if (dev < 0 || dev >= kMaxDevices) return query();
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    v = query();
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// The queries below fall back to a default when they fail and then clear the
+// error they left, so that the launcher's hipGetLastError() after its launch
+// reports only the launch.
+
+// Device a launch on `stream` runs on (the current device for the null
+// stream).
+inline int stream_device(hipStream_t stream) {
+  if (stream) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(stream, &d) == hipSuccess) return (int)d;
+    (void)hipGetLastError();
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) return dev;
+  (void)hipGetLastError();
+  return 0;
+}
+
+// Compute units of device `dev` (256, the MI355X count, if the query fails).
+inline int device_cus(int dev) {
+  static std::atomic<int> cache[kMaxDevices];
+  return per_device_cached(cache, dev, [dev] {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+      return c;
+    (void)hipGetLastError();
+    return 256;
+  });
+}
+
+// Resident blocks per CU of `kernel` at `threads` threads and no dynamic
+// LDS, on the current device (`fallback` if the query fails).
+inline int kernel_occupancy(const void* kernel, int threads, int fallback) {
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) == hipSuccess && occ > 0)
+    return occ;
+  (void)hipGetLastError();
+  return fallback;
+}
 
 // Descriptors per grouped launch (their block offsets travel in the kernel
 // argument block); longer lists are split into several launches.

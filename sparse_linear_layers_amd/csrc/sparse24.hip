@@ -563,19 +563,6 @@ __global__ __launch_bounds__(spws::NT, 1) void gemm_sp24_ws_kernel(Sp24Args a) {
   }
 }
 
-static int sp_num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
-}
-
 hipError_t launch_gemm_sparse24(const int8_t* xq, const float* beta, const void* sp,
                                 const void* scale, int scale_bf16, int64_t T, int64_t K, int64_t N,
                                 float* y, int32_t* acc, hipStream_t stream) {
@@ -586,10 +573,12 @@ hipError_t launch_gemm_sparse24(const int8_t* xq, const float* beta, const void*
   if (ws_o * ws_t > INT32_MAX) return hipErrorInvalidValue;
   // the warp-specialised kernel stores whole 16-byte pieces (N % 4 == 0) and
   // keeps 32-bit buffer offsets within a tile's rows of y
-  if (N % 4 == 0 && ws_o * ws_t >= sp_num_cus() && (int64_t)spws::BT * N * 4 < INT32_MAX / 2) {
+  const int dev = stream_device(stream);
+  const int cus = device_cus(dev);
+  if (N % 4 == 0 && ws_o * ws_t >= cus && (int64_t)spws::BT * N * 4 < INT32_MAX / 2) {
     a.tiles_o = (int)ws_o;
     a.ntiles = (int)(ws_o * ws_t);
-    const int grid = (int)std::min<int64_t>(a.ntiles, sp_num_cus());
+    const int grid = (int)std::min<int64_t>(a.ntiles, cus);
     if (scale_bf16)
       hipLaunchKernelGGL(gemm_sp24_ws_kernel<true>, dim3((unsigned)grid), dim3(spws::NT), 0, stream, a);
     else
@@ -598,11 +587,11 @@ hipError_t launch_gemm_sparse24(const int8_t* xq, const float* beta, const void*
   }
   a.tiles_o = (int)((N + BM - 1) / BM);
   a.ntiles = (int)((int64_t)a.tiles_o * ((T + BN - 1) / BN));
-  int occ = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_sp24_kernel<BM, BN>, 256, 0) !=
-          hipSuccess || occ < 1)
-    occ = 1;
-  const int grid = (int)std::min<int64_t>(a.ntiles, (int64_t)occ * sp_num_cus());
+  static std::atomic<int> occ_cache[kMaxDevices];
+  const int occ = per_device_cached(occ_cache, dev, [] {
+    return kernel_occupancy(reinterpret_cast<const void*>(gemm_sp24_kernel<BM, BN>), 256, 1);
+  });
+  const int grid = (int)std::min<int64_t>(a.ntiles, (int64_t)occ * cus);
   hipLaunchKernelGGL((gemm_sp24_kernel<BM, BN>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -320,19 +320,16 @@ __global__ __launch_bounds__(256) void ste_dw_reduce_kernel(const float* __restr
   }
 }
 
-// Blocks of the dw kernel resident at once on the current device.
+// Blocks of the dw kernel resident at once on the current device (the
+// workspace-size query has no stream, so both it and the launch use the
+// current device).
 static int64_t ste_slots() {
-  static int64_t slots = 0;
-  if (slots == 0) {
-    int dev = 0, cus = 0, occ = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ste_kernel<1>, ste::NT, 0) != hipSuccess || occ <= 0)
-      occ = 2;
-    slots = (int64_t)cus * occ;
-  }
-  return slots;
+  static std::atomic<int> occ_cache[kMaxDevices];
+  const int dev = stream_device(nullptr);
+  const int occ = per_device_cached(occ_cache, dev, [] {
+    return kernel_occupancy(reinterpret_cast<const void*>(ste_kernel<1>), ste::NT, 2);
+  });
+  return (int64_t)device_cus(dev) * occ;
 }
 
 // Split of the token reduction of dw: as many splits as fit the output
