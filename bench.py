@@ -19,8 +19,9 @@ passes included in the time).
 
 The same run also measures, outside the timed step and reported under
 "extra": each kernel's own rate against its roofline, the decode sweep
-(168 grouped GEMVs, batch 1/4/16, cold across rotated weight copies, replayed
-from a captured graph as a serving loop launches it), the
+(168 grouped GEMVs at 3:4 and at 2:4, batch 1/4/16, cold across rotated
+weight copies, replayed from a captured graph as a serving loop launches
+it), the
 2:4 smfmac product against the dense-expanded one, the 2048/7168 stack
 (full-model refresh and 8192-token products) and the tiny 256->512 layer.
 The CPU oracle is timed on a bounded sample of the step on the host cores.
@@ -340,53 +341,67 @@ def secondary(torch, sbl, synth, dev, timer):
     for layer in range(L):
         for name, N, K in synth.QWEN05B_LINEARS:
             mats.append((layer, name, N, K))
-    # latent weights -> packed codes on the GPU (one layer's worth at a time)
-    packed0, scales0 = [], []
+    # latent weights -> packed codes on the GPU at 3:4 and at 2:4 (one matrix
+    # at a time)
+    packed0 = {3: [], 2: []}
+    scales0 = {3: [], 2: []}
     for (layer, name, N, K) in mats:
         Wl = torch.from_numpy(synth.latent_weight(f"cfg4/L{layer}/{name}/W", N, K)).to(dev)
-        _, p, s, sb = sbl.nm_mask_quant_pack(Wl, 3, 4, want_mask=False)
-        packed0.append(p)
-        scales0.append(sb)
+        for nn in (3, 2):
+            _, p, s, sb = sbl.nm_mask_quant_pack(Wl, nn, 4, want_mask=False)
+            packed0[nn].append(p)
+            scales0[nn].append(sb)
         del Wl
     torch.cuda.synchronize()
-    # six copies of the whole packed set (6 x 90 MB > 2 x the 256 MB Infinity
-    # Cache) so that consecutive sweeps read weights from HBM
     ROT = 6
-    sets = [[p.clone() for p in packed0] for _ in range(ROT)]
-    code_bytes = sum(p.numel() for p in packed0)
-    dec = {}
+    x_by_B = {}
     for B in synth.DECODE_BATCHES:
         x_by_K = {}
         for K in (896, 4864):
             xb = torch.from_numpy(synth.activations_bf16(f"cfg4/x/{K}/B{B}", B, K).view(np.int16)).to(dev)
             x_by_K[K] = sbl.act_quant_i8(xb)
-        ys = [torch.empty((B, N), dtype=torch.float32, device=dev) for (_, _, N, _) in mats]
-        descs = []
-        for r in range(ROT):
-            jobs = [dict(xq=x_by_K[K][0], beta=x_by_K[K][1], packed=sets[r][i], scale=scales0[i],
-                         y=ys[i]) for i, (_, _, N, K) in enumerate(mats)]
-            descs.append(sbl.gemv_descs(jobs))
+        x_by_B[B] = x_by_K
 
-        def sweep(i=0, B=B, descs=descs):
-            h, d = descs[i % ROT]
-            sbl.sparse_bitlinear_gemv_grouped(h, d, len(mats), B, dev)
+    def decode_rates(nn):
+        # six copies of the whole packed set (6 x 90 MB > 2 x the 256 MB
+        # Infinity Cache) so that consecutive sweeps read weights from HBM
+        sets = [[p.clone() for p in packed0[nn]] for _ in range(ROT)]
+        code_bytes = sum(p.numel() for p in packed0[nn])
+        dec = {}
+        for B in synth.DECODE_BATCHES:
+            x_by_K = x_by_B[B]
+            ys = [torch.empty((B, N), dtype=torch.float32, device=dev) for (_, _, N, _) in mats]
+            descs = []
+            for r in range(ROT):
+                jobs = [dict(xq=x_by_K[K][0], beta=x_by_K[K][1], packed=sets[r][i],
+                             scale=scales0[nn][i], y=ys[i]) for i, (_, _, N, K) in enumerate(mats)]
+                descs.append(sbl.gemv_descs(jobs))
 
-        byts = code_bytes + sum(2 * N + B * K + 4 * B + 4 * B * N for (_, _, N, K) in mats)
-        # A decode step is launched from a captured graph in serving: the six
-        # rotated sweeps (one per weight copy, so each reads its weights from
-        # HBM) are captured once and replayed; the rate is per sweep.
-        us_graph = graph_time(torch, [lambda r=r: sweep(r) for r in range(ROT)], reps=20)
-        # eager single launches, for reference (each includes the host's
-        # submission latency when the device is idle)
-        med, mean = timer.time(sweep, 60, warmup=ROT)
-        medw, meanw = timer.time(lambda i=0: sweep(0), 30)
-        dec[f"B{B}"] = {"us": round(us_graph, 2), "gbs": round(byts / (us_graph * 1e-6) / 1e9, 1),
-                        "frac_hbm": round(byts / (us_graph * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                        "bytes": int(byts), "eager_us": round(mean * 1e3, 2),
-                        "eager_warm_us": round(meanw * 1e3, 2)}
-        log(f"[bench] decode B={B}: {dec[f'B{B}']}")
-    res["decode_sweep_3of4"] = dec
-    del sets, packed0
+            def sweep(i=0, B=B, descs=descs):
+                h, d = descs[i % ROT]
+                sbl.sparse_bitlinear_gemv_grouped(h, d, len(mats), B, dev)
+
+            byts = code_bytes + sum(2 * N + B * K + 4 * B + 4 * B * N for (_, _, N, K) in mats)
+            # A decode step is launched from a captured graph in serving: the
+            # six rotated sweeps (one per weight copy, so each reads its
+            # weights from HBM) are captured once and replayed; the rate is
+            # per sweep.
+            us_graph = graph_time(torch, [lambda r=r: sweep(r) for r in range(ROT)], reps=20)
+            # eager single launches, for reference (each includes the host's
+            # submission latency when the device is idle)
+            med, mean = timer.time(sweep, 60, warmup=ROT)
+            medw, meanw = timer.time(lambda i=0: sweep(0), 30)
+            dec[f"B{B}"] = {"us": round(us_graph, 2), "gbs": round(byts / (us_graph * 1e-6) / 1e9, 1),
+                            "frac_hbm": round(byts / (us_graph * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                            "bytes": int(byts), "eager_us": round(mean * 1e3, 2),
+                            "eager_warm_us": round(meanw * 1e3, 2)}
+            log(f"[bench] decode {nn}:4 B={B}: {dec[f'B{B}']}")
+        del sets
+        return dec
+
+    res["decode_sweep_3of4"] = decode_rates(3)
+    res["decode_sweep_2of4"] = decode_rates(2)
+    del packed0, scales0
     torch.cuda.empty_cache()
 
     # ---- 2:4: smfmac vs dense-expanded, identical seeded inputs ----
