@@ -447,6 +447,28 @@ def secondary(torch, sbl, synth, dev, timer):
     rb = 4.25 * nw + 4 * nr
     wide = {"refresh": {"weights": nw, "us": round(mr * 1e3, 1), "gbs": round(rb / (mr * 1e-3) / 1e9, 1),
                         "frac_hbm": round(rb / (mr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+    # the same refresh unfused: mask creation, then quantise + pack reading
+    # the mask back, per matrix (224 launches, replayed from a graph so that
+    # host submission is not what is timed)
+    lib = sbl.load()
+    mbuf = torch.empty(max(j["W"].numel() for j in jobs) // 8, dtype=torch.uint8, device=dev)
+
+    def unfused():
+        st = sbl._stream(dev)
+        for j in jobs:
+            rows, cols = j["W"].shape
+            e1 = lib.nm_mask_create(sbl._ptr(j["W"]), rows, cols, 3, 4, sbl._ptr(mbuf), st)
+            e2 = lib.ternary_quant_pack(sbl._ptr(j["W"]), sbl._ptr(mbuf), rows, cols, 0,
+                                        sbl._ptr(j["packed"]), sbl._ptr(j["scale"]), None, st)
+            if e1 or e2:
+                raise RuntimeError(f"unfused refresh: status {e1}, {e2}")
+
+    mu = graph_time(torch, [unfused], 5) * 1e-3
+    rbu = 8.5 * nw + 4 * nr
+    wide["refresh_unfused"] = {"us": round(mu * 1e3, 1), "gbs": round(rbu / (mu * 1e-3) / 1e9, 1),
+                               "frac_hbm": round(rbu / (mu * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                               "launches": 2 * len(jobs)}
+    del mbuf
     g = {}
     for name, N, K in synth.WIDE_LINEARS[3:]:  # o (2048x2048), gate, up, down
         j = jobs[[nm for nm, _, _ in synth.WIDE_LINEARS].index(name)]
