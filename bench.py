@@ -258,6 +258,9 @@ def main():
     med_a, mean_a = timer.time(lambda i=0: quant_acts(), 20)
     act_bytes = sum(3.0 * T * K + 4 * T for K in xin_K.values())
     extra = {
+        # ops at the kept weight positions only (n of every m), beside the
+        # dense-equivalent count that `value` uses
+        "useful_tops_n_over_m": round(tops * n / m, 2),
         "step_breakdown_us": {"refresh": round(mean_r * 1e3, 2), "act_quant": round(mean_a * 1e3, 2),
                               "gemm_total": round(tot_ms * 1e3, 2)},
         "gemm_per_shape": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
