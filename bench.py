@@ -275,6 +275,15 @@ def main():
 
     if not args.no_extra:
         extra.update(secondary(torch, sbl, synth, dev, timer))
+        # measured HBM ceilings for context: torch's own fill (write only)
+        # and device copy (read + write) of 1 GiB
+        buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        buf2 = torch.empty_like(buf)
+        _, mf = timer.time(lambda i=0: buf.fill_(1.0), 10)
+        _, mc = timer.time(lambda i=0: buf2.copy_(buf), 10)
+        extra["hbm_ceilings_1GiB"] = {"fill_gbs": round((1 << 30) / (mf * 1e-3) / 1e9, 1),
+                                      "copy_gbs": round((2 << 30) / (mc * 1e-3) / 1e9, 1)}
+        del buf, buf2
 
     cpu = None
     if not args.no_cpu_baseline:
