@@ -416,14 +416,24 @@ def secondary(torch, sbl, synth, dev, timer):
     del packed0, scales0
     torch.cuda.empty_cache()
 
-    # ---- 2:4: smfmac vs dense-expanded, identical seeded inputs ----
+    # ---- 2:4: smfmac vs dense-expanded, identical seeded inputs, on the
+    #      step's fused projections ----
     log("[bench] 2:4 products")
     T = synth.QWEN05B_PREFILL_TOKENS
+    dims = {name: (N, K) for name, N, K in synth.QWEN05B_LINEARS}
     sp = {}
     xcache = {}
-    for name, N, K in synth.QWEN05B_LINEARS:
-        Wl = torch.from_numpy(synth.latent_weight(f"cfg2/L0/{name}/W", N, K)).to(dev)
-        _, p, s, _ = sbl.nm_mask_quant_pack(Wl, 2, 4, want_mask=False, want_bf16=False)
+    for pname, members, _ in PROJECTIONS:
+        K = dims[members[0]][1]
+        parts = []
+        for mn in members:
+            Wl = torch.from_numpy(synth.latent_weight(f"cfg2/L0/{mn}/W", *dims[mn])).to(dev)
+            _, pm, sm, _ = sbl.nm_mask_quant_pack(Wl, 2, 4, want_mask=False, want_bf16=False)
+            parts.append((pm, sm))
+            del Wl
+        p = torch.cat([pm for pm, _ in parts]).contiguous()
+        s = torch.cat([sm for _, sm in parts]).contiguous()
+        N = p.shape[0]
         if K not in xcache:
             xb = torch.from_numpy(synth.activations_bf16(f"cfg3/x/{K}", T, K).view(np.int16)).to(dev)
             xcache[K] = sbl.act_quant_i8(xb)
@@ -433,10 +443,10 @@ def secondary(torch, sbl, synth, dev, timer):
         _, md = timer.time(lambda i=0: sbl.sparse_bitlinear_gemm(xqK, bK, p, s, y=yv), 10)
         _, ms = timer.time(lambda i=0: sbl.sparse_bitlinear_gemm_sparse24(xqK, bK, img, N, s, y=yv), 10)
         ops = 2.0 * T * N * K
-        sp[name] = {"dense_us": round(md * 1e3, 2), "smfmac_us": round(ms * 1e3, 2),
-                    "dense_tops": round(ops / (md * 1e-3) / 1e12, 1),
-                    "smfmac_tops": round(ops / (ms * 1e-3) / 1e12, 1)}
-        del Wl
+        sp[pname] = {"N": N, "K": K, "dense_us": round(md * 1e3, 2), "smfmac_us": round(ms * 1e3, 2),
+                     "dense_tops": round(ops / (md * 1e-3) / 1e12, 1),
+                     "smfmac_tops": round(ops / (ms * 1e-3) / 1e12, 1)}
+        del p, s, img, yv, parts
     res["prefill_2of4_smfmac_vs_dense"] = sp
     log(f"[bench] 2:4: {sp}")
     del xcache
