@@ -573,3 +573,19 @@ def test_repeat_runs_are_bitwise_identical(sbl):
     y1, a1 = sbl.sparse_bitlinear_gemm(*args, want_acc=True)
     y2, a2 = sbl.sparse_bitlinear_gemm(*args, want_acc=True)
     assert torch.equal(y1, y2) and torch.equal(a1, a2)
+
+
+def test_repeat_runs_of_the_large_tile_kernels_are_bitwise_identical(sbl):
+    """Two calls of the dense and the 2:4 large-tile products (at least one
+    256 x 256 tile per CU) give the same y and int32 accumulators bit for bit."""
+    T, K, N = 16384, 896, 1024
+    o = _operands("gpu/repeat_big", T, K, N, n=2, m=4)
+    xq, beta, packed, g = dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), dev(o["g"])
+    img = sbl.sparse24_compress(packed)
+    runs = [(sbl.sparse_bitlinear_gemm(xq, beta, packed, g, want_acc=True),
+             sbl.sparse_bitlinear_gemm_sparse24(xq, beta, img, N, g, want_acc=True)) for _ in range(2)]
+    (yd1, ad1), (ys1, as1) = runs[0]
+    (yd2, ad2), (ys2, as2) = runs[1]
+    assert torch.equal(yd1, yd2) and torch.equal(ad1, ad2)
+    assert torch.equal(ys1, ys2) and torch.equal(as1, as2)
+    assert torch.equal(yd1, ys1) and torch.equal(ad1, as1)
