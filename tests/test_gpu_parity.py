@@ -379,11 +379,13 @@ def test_sparse24_matches_dense(sbl, T, K, N):
     assert_y_close(host(y), oracle.dequant(acc_ref, o["beta"], o["g"]))
 
 
-@pytest.mark.parametrize("name,N,K", [("q", 896, 896), ("gate", 4864, 896), ("down", 896, 4864)])
+@pytest.mark.parametrize("name,N,K", [("q", 896, 896), ("gate", 4864, 896), ("down", 896, 4864),
+                                      ("qkv", 1152, 896), ("gate_up", 9728, 896)])
 def test_sparse24_full_size_sampled(sbl, name, N, K):
-    """The 2:4 product at the 0.5B skeleton's prefill size (32768 tokens), as
-    the benchmark runs it: acc and y on 96 sampled tokens against the
-    oracle, and y equal to the dense product's everywhere."""
+    """The 2:4 product at the 0.5B skeleton's prefill size (32768 tokens),
+    per linear and on the fused projections the benchmark times: acc and y
+    on 96 sampled tokens against the oracle, and y equal to the dense
+    product's everywhere."""
     T = synth.QWEN05B_PREFILL_TOKENS
     W = synth.latent_weight(f"gpu/sp24full/{name}/W", N, K)
     x = synth.activations_bf16(f"gpu/sp24full/{name}/x", T, K)
@@ -401,8 +403,9 @@ def test_sparse24_full_size_sampled(sbl, name, N, K):
     rows = np.sort(synth.rng(f"gpu/sp24full/{name}/sample").choice(T, 96, replace=False))
     rows[-1] = T - 1
     acc_ref = oracle.gemm_acc(xq[rows], codes)
-    assert np.array_equal(host(acc)[rows], acc_ref)
-    assert_y_close(host(y)[rows], oracle.dequant(acc_ref, beta[rows], g))
+    rows_d = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(host(acc[rows_d]), acc_ref)
+    assert_y_close(host(y[rows_d]), oracle.dequant(acc_ref, beta[rows], g))
 
 
 @pytest.mark.parametrize("T,K,N,bf16_scale", [(16400, 320, 1000, False), (16400, 192, 1004, True),
@@ -495,11 +498,11 @@ def test_gemv_grouped(sbl, T):
         assert_y_close(host(j["y"]), oracle.dequant(acc_ref, o["beta"], g))
 
 
-@pytest.mark.parametrize("T", [1, 16])
-def test_gemv_grouped_full_sweep(sbl, T):
+@pytest.mark.parametrize("T,n", [(1, 3), (16, 3), (1, 2)])
+def test_gemv_grouped_full_sweep(sbl, T, n):
     """The decode sweep as the benchmark launches it: all 168 linears of the
     0.5B skeleton (24 layers x 7) in one grouped call, bf16 row scales, one
-    x~ per input width; every output against the oracle."""
+    x~ per input width, at 3:4 and at 2:4; every output against the oracle."""
     K_in = {"q": 896, "k": 896, "v": 896, "o": 896, "gate": 896, "up": 896, "down": 4864}
     xs = {}
     for K in (896, 4864):
@@ -511,7 +514,7 @@ def test_gemv_grouped_full_sweep(sbl, T):
         for name, N, K in synth.QWEN05B_LINEARS:
             W = synth.latent_weight(f"gpu/gemvsweep/L{layer}/{name}", N, K)
             g, gb = oracle.row_scale(W)
-            codes = oracle.ternary_codes(W, oracle.nm_mask(W, 3, 4), g)
+            codes = oracle.ternary_codes(W, oracle.nm_mask(W, n, 4), g)
             jobs.append(dict(xq=xd[K][0], beta=xd[K][1], packed=dev(oracle.pack_codes(codes)),
                              scale=dev(gb), y=torch.full((T, N), float("nan"), device=DEV)))
             refs.append((codes, oracle.bf16_bits_to_float(gb), K))
