@@ -205,6 +205,25 @@ int nm_mask_stats(const uint8_t* old_bits, const uint8_t* new_bits, int64_t rows
                   int64_t cols, int n, int m, int64_t* stats, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Packed-code validator.
+ * Model card "Packed vs raw": a weight is stored as one of the 2-bit codes
+ * 00 (0), 01 (+1), 10 (-1), so the field 11 never occurs in a valid matrix;
+ * model card "Recipe" and README "N:M Structured Sparsity": under an n:m
+ * mask every group of m consecutive weights of a row holds at most n
+ * nonzeros (codes may add zeros inside the kept positions).
+ *   stats[0] = number of 2-bit fields equal to 11 (the products read them
+ *              as 0)
+ *   stats[1] = number of m-groups of a row with more than n codes 01 or 10
+ *   packed  uint8 [rows, cols/4] (layout of ternary_quant_pack); may be
+ *           NULL when rows is 0 (the counts are then zeroed)
+ *   n, m    m in {4, 8}, 0 <= n <= m
+ *   stats   int64 [2], device memory, 8-byte aligned; overwritten (zeroed by
+ *           the call itself before counting)
+ * ------------------------------------------------------------------------ */
+int packed_codes_check(const uint8_t* packed, int64_t rows, int64_t cols, int n, int m,
+                       int64_t* stats, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Packed-ternary x int8 product, prefill (dense int8 matrix cores).
  * Guide "Mathematical Formulation", step 4 (integer product, rescale).
  *   acc[t, o] = sum_k xq[t, k] * code[o, k]   (int32, exact)
@@ -244,14 +263,20 @@ int sparse_bitlinear_gemm_sparse24(const int8_t* xq, const float* beta,
 
 /* ------------------------------------------------------------------------
  * Decode product (GEMV), 1 <= T <= 16 tokens; same contract as
- * sparse_bitlinear_gemm.  Model card "What does NOT ship" (the serve path
- * needs a kernel that reads the packed layout directly).
+ * sparse_bitlinear_gemm, including the optional int32 accumulators.
+ * Model card "What does NOT ship" (the serve path needs a kernel that reads
+ * the packed layout directly).  Up to 4 tokens run on the vector ALU
+ * (int8 dot products), more on the int8 matrix cores; both give the same
+ * exact acc and y.
+ * Errors: SBL_ERR_UNSUPPORTED for T outside [1, 16]; SBL_ERR_SHAPE for
+ * N > SBL_GEMV_MAX_ROWS.
  * ------------------------------------------------------------------------ */
 #define SBL_GEMV_MAX_TOKENS 16
+#define SBL_GEMV_MAX_ROWS (1 << 28)
 int sparse_bitlinear_gemv(const int8_t* xq, const float* beta,
                           const uint8_t* packed, const void* row_scale,
                           int scale_dtype, int64_t T, int64_t K, int64_t N,
-                          float* y, hipStream_t stream);
+                          float* y, int32_t* acc, hipStream_t stream);
 
 /* Many decode products in one launch (for example every linear of every
  * layer).  Host and device copies of the same descriptors, as for
@@ -262,6 +287,7 @@ typedef struct sbl_gemv_desc {
   const uint8_t* packed;  /* uint8 [N, K/4]                       */
   const void* row_scale;  /* float or bf16 [N], per scale_dtype   */
   float* y;               /* float [T, N]                         */
+  int32_t* acc;           /* int32 [T, N] or NULL                 */
   int64_t K;
   int64_t N;
   int32_t scale_dtype;    /* SBL_SCALE_F32 or SBL_SCALE_BF16      */

@@ -27,6 +27,10 @@ something other than itself; the tests named are under ``tests/``):
                      table; round trip; total size of the 0.5B skeleton's
                      packed state matching the card's 346 MB
                      (test_oracle_pack.py).
+* ``packed_check``   pure-Python bit loops over every byte value; codes
+                     packed from n:m-masked ternary weights validate clean;
+                     planted 11 fields and over-full groups counted exactly;
+                     a hand-decoded byte (test_oracle_pack.py).
 * ``act_quant``      exact rational |x~ - x*127/beta| <= 1/2 (+ float slack);
                      argmax element maps to +-127; zero token; scaling x by
                      a power of two leaves x~ unchanged (test_oracle_act.py).
@@ -50,8 +54,9 @@ something other than itself; the tests named are under ``tests/``):
                      gradient entry (test_oracle_ste.py).
 * ``dequant``        exact rational product rounded to float
                      (test_oracle_gemm.py); whole-layer cross-check against
-                     a float64 re-statement of the guide's PyTorch module with
-                     per-row gamma and no RMSNorm (test_oracle_layer.py).
+                     a numpy statement of the guide's formulation (stable-sort
+                     mask, closed-form codes, int64 product) with per-row
+                     gamma and no RMSNorm (test_oracle_layer.py).
 """
 from __future__ import annotations
 
@@ -111,6 +116,7 @@ def _load():
     lib.oracle_dequant.argtypes = [P, P, P, I64, I64, P]
     lib.oracle_rmsnorm_act_quant.argtypes = [P, P, ctypes.c_float, I64, I64, P, P, P]
     lib.oracle_mask_stats.argtypes = [P, P, I64, I64, I, I, P]
+    lib.oracle_packed_check.argtypes = [P, I64, I64, I, I, P]
     lib.oracle_tensor_scale.argtypes = [P, P, I, I64, I64]
     lib.oracle_tensor_scale.restype = ctypes.c_float
     lib.oracle_ste_backward.argtypes = [P, P, P, P, P, I64, I64, I64, P, P]
@@ -193,6 +199,15 @@ def unpack_codes(packed: np.ndarray, cols: int) -> np.ndarray:
     out = np.empty((rows, cols), dtype=np.int8)
     _load().oracle_unpack_codes(_ptr(packed), rows, cols, _ptr(out))
     return out
+
+
+def packed_check(packed: np.ndarray, cols: int, n: int, m: int) -> tuple[int, int]:
+    """(fields equal to 11, m-groups with more than n nonzero codes)."""
+    p = _c(packed, np.uint8)
+    rows = p.shape[0]
+    out = np.zeros(2, np.int64)
+    _load().oracle_packed_check(_ptr(p), rows, cols, n, m, _ptr(out))
+    return int(out[0]), int(out[1])
 
 
 def act_quant(x_bf16: np.ndarray):

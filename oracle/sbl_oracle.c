@@ -189,6 +189,34 @@ void oracle_unpack_codes(const uint8_t* packed, int64_t rows, int64_t cols,
 }
 
 /* ------------------------------------------------------------------------ *
+ * Packed-code validator.  [halo] "Packed vs raw": the 2-bit fields 00, 01
+ * and 10 are the codes 0, +1 and -1, so 11 is no code at all; [halo]
+ * "Recipe" and [repo] "N:M Structured Sparsity": under an n:m mask at most
+ * n of every m consecutive weights of a row are nonzero.
+ * stats[0] = number of fields equal to 11; stats[1] = number of m-groups of
+ * a row holding more than n fields equal to 01 or 10.
+ * ------------------------------------------------------------------------ */
+void oracle_packed_check(const uint8_t* packed, int64_t rows, int64_t cols,
+                         int n, int m, int64_t* stats) {
+  int64_t bpr = cols / 4, not_code = 0, over_n = 0;
+#pragma omp parallel for schedule(static) reduction(+ : not_code, over_n)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t g = 0; g < cols / m; ++g) {
+      int nonzero = 0;
+      for (int i = 0; i < m; ++i) {
+        int64_t j = g * m + i;
+        unsigned f = (packed[r * bpr + j / 4] >> (2 * (j % 4))) & 3u;
+        if (f == 3u) not_code++;
+        else if (f != 0u) nonzero++;
+      }
+      if (nonzero > n) over_n++;
+    }
+  }
+  stats[0] = not_code;
+  stats[1] = over_n;
+}
+
+/* ------------------------------------------------------------------------ *
  * Per-token absmax int8 activation quantisation.
  * [guide] item 4: beta = max_j |x_j|, x~ = Clip(Round(x * 127/beta), -128, 127);
  * the module clamps beta below at 1e-5 and scales by (127/beta) computed

@@ -28,7 +28,7 @@ __all__ = [
     "sparse_bitlinear_gemm_sparse24", "sparse_bitlinear_gemv",
     "sparse_bitlinear_gemv_grouped", "GemvDesc", "RefreshDesc", "refresh_descs", "gemv_descs",
     "SCALE_FROM_MASKED", "SCALE_PER_TENSOR", "SCALE_F32", "SCALE_BF16", "GEMV_MAX_TOKENS",
-    "rmsnorm_act_quant_i8", "nm_mask_stats", "sparse_bitlinear_ste_backward",
+    "rmsnorm_act_quant_i8", "nm_mask_stats", "packed_codes_check", "sparse_bitlinear_ste_backward",
     "sparse_bitlinear_ste_workspace_bytes",
 ]
 
@@ -37,6 +37,7 @@ SCALE_PER_TENSOR = 2
 SCALE_F32 = 0
 SCALE_BF16 = 1
 GEMV_MAX_TOKENS = 16
+GEMV_MAX_ROWS = 1 << 28
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libsbl.so")
@@ -63,8 +64,8 @@ class RefreshDesc(ctypes.Structure):
 class GemvDesc(ctypes.Structure):
     _fields_ = [("xq", ctypes.c_void_p), ("beta", ctypes.c_void_p),
                 ("packed", ctypes.c_void_p), ("row_scale", ctypes.c_void_p),
-                ("y", ctypes.c_void_p), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
-                ("scale_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("y", ctypes.c_void_p), ("acc", ctypes.c_void_p), ("K", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("scale_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 def load() -> ctypes.CDLL:
@@ -86,12 +87,13 @@ def load() -> ctypes.CDLL:
         "act_quant_i8": [P, I64, I64, P, P, P],
         "rmsnorm_act_quant_i8": [P, P, ctypes.c_float, I64, I64, P, P, P],
         "nm_mask_stats": [P, P, I64, I64, I, I, P, P],
+        "packed_codes_check": [P, I64, I64, I, I, P, P],
         "sparse_bitlinear_ste_backward": [P, P, P, P, P, I64, I64, I64, P, P, P,
                                           ctypes.c_size_t, P],
         "sparse_bitlinear_gemm": [P, P, P, P, I, I64, I64, I64, P, P, P],
         "sparse24_compress": [P, I64, I64, P, P, P],
         "sparse_bitlinear_gemm_sparse24": [P, P, P, P, I, I64, I64, I64, P, P, P],
-        "sparse_bitlinear_gemv": [P, P, P, P, I, I64, I64, I64, P, P],
+        "sparse_bitlinear_gemv": [P, P, P, P, I, I64, I64, I64, P, P, P],
         "sparse_bitlinear_gemv_grouped": [P, P, I, I64, P],
     }
     for name, args in sig.items():
@@ -278,6 +280,21 @@ def nm_mask_stats(old_bits: torch.Tensor | None, new_bits: torch.Tensor, rows: i
     return stats
 
 
+def packed_codes_check(packed: torch.Tensor, n: int, m: int,
+                       stats: torch.Tensor | None = None) -> torch.Tensor:
+    """Validator of packed codes [rows, cols/4] as an int64 device tensor
+    [2]: 2-bit fields equal to 11 (not a code), and m-groups of a row holding
+    more than n nonzero codes."""
+    _need(packed, torch.uint8, "packed", 2)
+    rows, cols = packed.shape[0], packed.shape[1] * 4
+    if stats is None:
+        stats = torch.empty(2, dtype=torch.int64, device=packed.device)
+    _shape(stats, (2,), torch.int64, "stats")
+    _check("packed_codes_check", load().packed_codes_check(
+        _ptr(packed), rows, cols, n, m, _ptr(stats), _stream(packed.device)))
+    return stats
+
+
 def sparse_bitlinear_ste_workspace_bytes(T: int, K: int, N: int) -> int:
     return int(load().sparse_bitlinear_ste_workspace_bytes(T, K, N))
 
@@ -366,11 +383,25 @@ def sparse24_bytes(N: int, K: int) -> int:
 
 def sparse24_compress(packed: torch.Tensor, bad_groups: torch.Tensor | None = None,
                       out: torch.Tensor | None = None):
-    """packed uint8 [N, K/4] (2:4 codes) -> private smfmac operand image."""
+    """packed uint8 [N, K/4] (2:4 codes) -> private smfmac operand image
+    (uint8, at least sparse24_bytes(N, K) bytes).  `bad_groups` (int32 [>= 1]
+    on the same device, zeroed by the caller) counts groups of 4 codes that
+    hold more than 2 nonzeros."""
     _need(packed, torch.uint8, "packed", 2)
     N, K = packed.shape[0], packed.shape[1] * 4
     if out is None:
         out = torch.empty(max(sparse24_bytes(N, K), 16), dtype=torch.uint8, device=packed.device)
+    _need(out, torch.uint8, "out")
+    if out.device != packed.device:
+        raise ValueError(f"out: must live on {packed.device}, got {out.device}")
+    if out.numel() < sparse24_bytes(N, K):
+        raise ValueError("out: smaller than sparse24_bytes(N, K)")
+    if bad_groups is not None:
+        _need(bad_groups, torch.int32, "bad_groups")
+        if bad_groups.device != packed.device:
+            raise ValueError(f"bad_groups: must live on {packed.device}, got {bad_groups.device}")
+        if bad_groups.numel() < 1:
+            raise ValueError("bad_groups: needs at least one element")
     _check("sparse24_compress", load().sparse24_compress(
         _ptr(packed), N, K, _ptr(out), _ptr(bad_groups), _stream(packed.device)))
     return out
@@ -398,7 +429,10 @@ def sparse_bitlinear_gemm_sparse24(xq, beta, sp24, N: int, scale, want_acc: bool
     return y, acc
 
 
-def sparse_bitlinear_gemv(xq, beta, packed, scale, y: torch.Tensor | None = None):
+def sparse_bitlinear_gemv(xq, beta, packed, scale, y: torch.Tensor | None = None,
+                          want_acc: bool = False):
+    """Decode product, 1 <= T <= 16 tokens -> y float32 [T, N] (and the
+    int32 accumulators [T, N] when want_acc: then a tuple (y, acc))."""
     _need(xq, torch.int8, "xq", 2)
     _need(beta, torch.float32, "beta", 1)
     _need(packed, torch.uint8, "packed", 2)
@@ -413,15 +447,17 @@ def sparse_bitlinear_gemv(xq, beta, packed, scale, y: torch.Tensor | None = None
     if y is None:
         y = torch.empty((T, N), dtype=torch.float32, device=dev)
     _shape(y, (T, N), torch.float32, "y")
+    acc = torch.empty((T, N), dtype=torch.int32, device=dev) if want_acc else None
     _check("sparse_bitlinear_gemv", load().sparse_bitlinear_gemv(
         _ptr(xq), _ptr(beta), _ptr(packed), _ptr(scale), _scale_dtype(scale), T, K, N,
-        _ptr(y), _stream(dev)))
-    return y
+        _ptr(y), _ptr(acc), _stream(dev)))
+    return (y, acc) if want_acc else y
 
 
 def gemv_descs(jobs):
     """Build (host array, device tensor) descriptors for
-    sparse_bitlinear_gemv_grouped from dicts with xq, beta, packed, scale, y."""
+    sparse_bitlinear_gemv_grouped from dicts with xq, beta, packed, scale, y
+    and an optional int32 acc [T, N]."""
     dev = jobs[0]["xq"].device
     ds = []
     if len({j["xq"].shape[0] for j in jobs}) > 1:
@@ -437,9 +473,13 @@ def gemv_descs(jobs):
         _shape(j["beta"], (T,), torch.float32, "beta")
         _shape(scale, (N,), None, "scale")
         _shape(j["y"], (T, N), torch.float32, "y")
+        acc = j.get("acc")
+        if acc is not None:
+            _shape(acc, (T, N), torch.int32, "acc")
         ds.append(GemvDesc(xq.data_ptr(), j["beta"].data_ptr(), packed.data_ptr(),
-                           scale.data_ptr(), j["y"].data_ptr(), xq.shape[1], packed.shape[0],
-                           _scale_dtype(scale), 0))
+                           scale.data_ptr(), j["y"].data_ptr(),
+                           acc.data_ptr() if acc is not None else None, xq.shape[1],
+                           packed.shape[0], _scale_dtype(scale), 0))
     return _desc_array(ds, GemvDesc, dev)
 
 

@@ -142,6 +142,17 @@ int nm_mask_stats(const uint8_t* old_bits, const uint8_t* new_bits, int64_t rows
   return hip_status(sbl::launch_mask_stats(old_bits, new_bits, rows, cols, n, m, stats, stream));
 }
 
+int packed_codes_check(const uint8_t* packed, int64_t rows, int64_t cols, int n, int m,
+                       int64_t* stats, hipStream_t stream) {
+  if (rows < 0 || rows > kMaxRows) return SBL_ERR_ARG;
+  if (int s = check_cols(cols)) return s;
+  if (int s = check_nm(n, m)) return s;
+  if (!stats || (rows > 0 && !packed)) return SBL_ERR_ARG;
+  if (!aligned16_or_null(packed) || (reinterpret_cast<uintptr_t>(stats) & 7u)) return SBL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(sbl::launch_packed_check(packed, rows, cols, n, m, stats, stream));
+}
+
 int act_quant_i8(const uint16_t* x_bf16, int64_t tokens, int64_t cols, int8_t* xq, float* beta,
                  hipStream_t stream) {
   if (tokens < 0 || tokens > kMaxRows) return SBL_ERR_ARG;
@@ -208,11 +219,12 @@ int sparse_bitlinear_gemm_sparse24(const int8_t* xq, const float* beta, const vo
 
 int sparse_bitlinear_gemv(const int8_t* xq, const float* beta, const uint8_t* packed,
                           const void* row_scale, int scale_dtype, int64_t T, int64_t K, int64_t N,
-                          float* y, hipStream_t stream) {
+                          float* y, int32_t* acc, hipStream_t stream) {
   if (T < 1 || T > SBL_GEMV_MAX_TOKENS) return SBL_ERR_UNSUPPORTED;
-  if (int s = check_product(xq, beta, packed, row_scale, scale_dtype, T, K, N, y, nullptr)) return s;
+  if (int s = check_product(xq, beta, packed, row_scale, scale_dtype, T, K, N, y, acc)) return s;
+  if (N > SBL_GEMV_MAX_ROWS) return SBL_ERR_SHAPE;
   if (N == 0) return SBL_OK;
-  sbl_gemv_desc d{xq, beta, packed, row_scale, y, K, N, scale_dtype, 0};
+  sbl_gemv_desc d{xq, beta, packed, row_scale, y, acc, K, N, scale_dtype, 0};
   (void)hipGetLastError();
   return hip_status(sbl::launch_gemv(&d, nullptr, 1, T, stream));
 }
@@ -227,8 +239,9 @@ int sparse_bitlinear_gemv_grouped(const sbl_gemv_desc* descs_host, const sbl_gem
   for (int i = 0; i < count; ++i) {
     const sbl_gemv_desc& d = descs_host[i];
     if (int s = check_product(d.xq, d.beta, d.packed, d.row_scale, d.scale_dtype, T, d.K, d.N, d.y,
-                              nullptr))
+                              d.acc))
       return s;
+    if (d.N > SBL_GEMV_MAX_ROWS) return SBL_ERR_SHAPE;
     if (d.reserved != 0) return SBL_ERR_ARG;
     blocks += sbl::gemv_blocks(d.N, T);
   }

@@ -84,6 +84,8 @@ hipError_t launch_quant_pack_grouped(const sbl_refresh_desc* host, const sbl_ref
                                      int count, int n, int m, unsigned flags, hipStream_t stream);
 hipError_t launch_mask_stats(const uint8_t* old_bits, const uint8_t* new_bits, int64_t rows,
                              int64_t cols, int n, int m, int64_t* stats, hipStream_t stream);
+hipError_t launch_packed_check(const uint8_t* packed, int64_t rows, int64_t cols, int n, int m,
+                               int64_t* stats, hipStream_t stream);
 hipError_t launch_rmsnorm_act_quant(const uint16_t* x, const float* w, float eps, int64_t tokens,
                                     int64_t cols, int8_t* xq, float* beta, hipStream_t stream);
 hipError_t launch_act_quant(const uint16_t* x, int64_t tokens, int64_t cols, int8_t* xq,
@@ -101,7 +103,7 @@ hipError_t launch_ste_backward(const float* dy, const int8_t* xq, const float* b
                                const uint8_t* packed, const float* gamma, int64_t T, int64_t K,
                                int64_t N, float* dx, float* dw, void* workspace,
                                hipStream_t stream);
-int64_t gemv_blocks(int64_t N, int64_t T);  // blocks of the decode product over N rows
+int64_t gemv_blocks(int64_t N, int64_t T);  // work units of the decode product over N rows
 hipError_t launch_gemv(const sbl_gemv_desc* host, const sbl_gemv_desc* dev_or_null, int count,
                        int64_t T, hipStream_t stream);
 

@@ -405,25 +405,57 @@ __device__ __forceinline__ uint4 load_u4_stream(const uint4* p, int64_t idx) {
   return make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
 }
 
+// Per-word counters of the two stream kernels below.  `a` is a word of
+// the stream that is checked, `b` the matching word of the second stream
+// (the old mask; equal to `a` when there is none).
+template <int M>
+struct MaskStatsOp {
+  __device__ __forceinline__ static void word(uint32_t a, uint32_t b, uint32_t n, uint32_t& c0, uint32_t& c1) {
+    c0 += (uint32_t)__popc(a ^ b);
+    c1 += groups_not_n<M>(a, n);
+  }
+};
+
+// Packed-code validator (model card "Packed vs raw": the field 11 is not a
+// code; "Recipe": at most n nonzero codes per group of m).  A 32-bit word
+// holds 16 fields; with lo/hi the low and high bit of every field, 11 is
+// lo & hi and a nonzero code (01 or 10) is lo ^ hi.  Groups of 4 fields are
+// the bytes of the word, groups of 8 its 16-bit halves, so no group
+// straddles two words (a row is a whole number of 16-byte chunks).
+template <int M>
+struct PackedCheckOp {
+  __device__ __forceinline__ static void word(uint32_t a, uint32_t, uint32_t n, uint32_t& c0, uint32_t& c1) {
+    const uint32_t lo = a & 0x55555555u, hi = (a >> 1) & 0x55555555u;
+    c0 += (uint32_t)__popc(lo & hi);
+    const uint32_t nz = lo ^ hi;
+    uint32_t v = (nz & 0x33333333u) + ((nz >> 2) & 0x33333333u);  // per 4 bits: 0..2
+    v = (v + (v >> 4)) & 0x0F0F0F0Fu;                              // per byte: 0..4
+    if constexpr (M == 4) {
+      // byte + (127 - n) reaches bit 7 iff the byte's count exceeds n
+      c1 += (uint32_t)__popc((v + (0x7Fu - n) * 0x01010101u) & 0x80808080u);
+    } else {
+      v = (v + (v >> 8)) & 0x001F001Fu;                            // per 16 bits: 0..8
+      c1 += (uint32_t)__popc((v + (0x7FFFu - n) * 0x00010001u) & 0x80008000u);
+    }
+  }
+};
+
 // One block of 1024 threads per CU at most: few blocks keep the two 64-bit
 // atomics per block cheap (they serialise on one address), and four 16-byte
 // loads per operand and lane keep enough bytes in flight.
 constexpr int kStatsThreads = 1024;
 
-template <int M>
-__global__ __launch_bounds__(kStatsThreads) void mask_stats_kernel(const uint32_t* __restrict__ old_w,
+template <typename Op>
+__global__ __launch_bounds__(kStatsThreads) void word_stats_kernel(const uint32_t* __restrict__ old_w,
                                                                    const uint32_t* __restrict__ new_w,
                                                                    int64_t words, int n,
                                                                    unsigned long long* stats) {
   __shared__ unsigned long long part[2][kStatsThreads / kWave];
-  uint32_t changed = 0, bad = 0;
+  uint32_t c0 = 0, c1 = 0;
   const int64_t nvec = words >> 2;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t gsz = (int64_t)gridDim.x * blockDim.x;
-  auto word = [&](uint32_t a, uint32_t b) {
-    changed += (uint32_t)__popc(a ^ b);
-    bad += groups_not_n<M>(a, (uint32_t)n);
-  };
+  auto word = [&](uint32_t a, uint32_t b) { Op::word(a, b, (uint32_t)n, c0, c1); };
   const uint4* nv = reinterpret_cast<const uint4*>(new_w);
   const uint4* ov = reinterpret_cast<const uint4*>(old_w);
   int64_t i = gid;
@@ -451,9 +483,9 @@ __global__ __launch_bounds__(kStatsThreads) void mask_stats_kernel(const uint32_
     word(a.w, b.w);
   }
   for (int64_t i = 4 * nvec + gid; i < words; i += gsz) word(new_w[i], old_w ? old_w[i] : new_w[i]);
-  // A lane's counts stay below 2^32 (at most 2^46 mask bits over 2^18
-  // lanes); wave and block sums are 64-bit, then one atomic per counter.
-  unsigned long long c64 = changed, g64 = bad;
+  // A lane's counts stay below 2^32 (at most 2^46 bits over 2^18 lanes);
+  // wave and block sums are 64-bit, then one atomic per counter.
+  unsigned long long c64 = c0, g64 = c1;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
     c64 += (unsigned long long)__shfl_xor((long long)c64, d, kWave);
@@ -559,20 +591,35 @@ static void launch_grouped(int cpl, dim3 grid, hipStream_t stream, const Grouped
   }
 }
 
-hipError_t launch_mask_stats(const uint8_t* old_bits, const uint8_t* new_bits, int64_t rows,
-                             int64_t cols, int n, int m, int64_t* stats, hipStream_t stream) {
+// Zero the two counters, then one pass of word_stats_kernel<Op> over
+// `words` 32-bit words.
+template <template <int> class Op>
+static hipError_t launch_word_stats(const uint32_t* ow, const uint32_t* nw, int64_t words, int n, int m,
+                                    int64_t* stats, hipStream_t stream) {
   unsigned long long* st = reinterpret_cast<unsigned long long*>(stats);
   hipLaunchKernelGGL(zero_stats_kernel, dim3(1), dim3(64), 0, stream, st);
-  const int64_t words = rows * cols / 32;
-  const int64_t blocks =
-      std::max<int64_t>(1, std::min<int64_t>((words / 16 + kStatsThreads - 1) / kStatsThreads, 256));
-  const uint32_t* ow = reinterpret_cast<const uint32_t*>(old_bits);
-  const uint32_t* nw = reinterpret_cast<const uint32_t*>(new_bits);
-  if (m == 4)
-    hipLaunchKernelGGL(mask_stats_kernel<4>, dim3((unsigned)blocks), dim3(kStatsThreads), 0, stream, ow, nw, words, n, st);
-  else
-    hipLaunchKernelGGL(mask_stats_kernel<8>, dim3((unsigned)blocks), dim3(kStatsThreads), 0, stream, ow, nw, words, n, st);
+  if (words > 0) {
+    const int64_t blocks =
+        std::max<int64_t>(1, std::min<int64_t>((words / 16 + kStatsThreads - 1) / kStatsThreads, 256));
+    if (m == 4)
+      hipLaunchKernelGGL(word_stats_kernel<Op<4>>, dim3((unsigned)blocks), dim3(kStatsThreads), 0, stream, ow, nw, words, n, st);
+    else
+      hipLaunchKernelGGL(word_stats_kernel<Op<8>>, dim3((unsigned)blocks), dim3(kStatsThreads), 0, stream, ow, nw, words, n, st);
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_mask_stats(const uint8_t* old_bits, const uint8_t* new_bits, int64_t rows,
+                             int64_t cols, int n, int m, int64_t* stats, hipStream_t stream) {
+  return launch_word_stats<MaskStatsOp>(reinterpret_cast<const uint32_t*>(old_bits),
+                                        reinterpret_cast<const uint32_t*>(new_bits), rows * cols / 32, n, m,
+                                        stats, stream);
+}
+
+hipError_t launch_packed_check(const uint8_t* packed, int64_t rows, int64_t cols, int n, int m,
+                               int64_t* stats, hipStream_t stream) {
+  return launch_word_stats<PackedCheckOp>(nullptr, reinterpret_cast<const uint32_t*>(packed),
+                                          rows * cols / 16, n, m, stats, stream);
 }
 
 hipError_t launch_quant_pack_grouped(const sbl_refresh_desc* host, const sbl_refresh_desc* dev,

@@ -83,9 +83,11 @@ def test_product_validation(lib):
     assert f(P, P, P, P, 0, 0, 64, 8, P, None, None) == OK
     assert f(P, P, P, P, 0, 8, 64, 0, P, None, None) == OK
     v = lib.sparse_bitlinear_gemv
-    assert v(P, P, P, P, 0, 0, 64, 8, P, None) == UNSUP
-    assert v(P, P, P, P, 0, 17, 64, 8, P, None) == UNSUP
-    assert v(P, P, P, P, 1, 1, 64, 0, P, None) == OK
+    assert v(P, P, P, P, 0, 0, 64, 8, P, None, None) == UNSUP
+    assert v(P, P, P, P, 0, 17, 64, 8, P, None, None) == UNSUP
+    assert v(P, P, P, P, 1, 1, 64, 0, P, None, None) == OK
+    assert v(P, P, P, P, 1, 1, 64, 8, P, MIS, None) == ALIGN      # int32 accumulators
+    assert v(P, P, P, P, 1, 1, 64, (1 << 28) + 1, P, None, None) == SHAPE
     s = lib.sparse_bitlinear_gemm_sparse24
     assert s(P, P, None, P, 0, 8, 64, 8, P, None, None) == ARG
     assert lib.sparse24_compress(P, 8, 64, P, MIS + 2, None) == ALIGN
@@ -94,13 +96,19 @@ def test_product_validation(lib):
 
 
 def test_grouped_validation(lib):
-    d = (sbl.GemvDesc * 2)(sbl.GemvDesc(P, P, P, P, P, 64, 8, 0, 0),
-                           sbl.GemvDesc(P, P, P, P, P, 96, 8, 0, 0))
+    d = (sbl.GemvDesc * 2)(sbl.GemvDesc(P, P, P, P, P, None, 64, 8, 0, 0),
+                           sbl.GemvDesc(P, P, P, P, P, None, 96, 8, 0, 0))
     hp = ctypes.cast(d, ctypes.c_void_p)
     assert lib.sparse_bitlinear_gemv_grouped(hp, P, 2, 1, None) == SHAPE
     assert lib.sparse_bitlinear_gemv_grouped(hp, P, 0, 1, None) == OK
     assert lib.sparse_bitlinear_gemv_grouped(hp, None, 2, 1, None) == ARG
     assert lib.sparse_bitlinear_gemv_grouped(hp, P, 1, 20, None) == UNSUP
+    d[0].acc = MIS
+    assert lib.sparse_bitlinear_gemv_grouped(hp, P, 1, 1, None) == ALIGN
+    d[0].acc, d[0].N = None, (1 << 28) + 4
+    assert lib.sparse_bitlinear_gemv_grouped(hp, P, 1, 1, None) == SHAPE
+    d[0].N, d[0].reserved = 8, 1
+    assert lib.sparse_bitlinear_gemv_grouped(hp, P, 1, 1, None) == ARG
     r = (sbl.RefreshDesc * 1)(sbl.RefreshDesc(P, None, P, P, MIS, 4, 64))
     assert lib.nm_mask_quant_pack_grouped(ctypes.cast(r, ctypes.c_void_p), P, 1, 3, 4, 0, None) == ALIGN
     assert lib.nm_mask_quant_pack_grouped(ctypes.cast(r, ctypes.c_void_p), P, 1, 3, 5, 0, None) == UNSUP
@@ -180,3 +188,25 @@ def test_ste_backward_validation(lib):
     assert f(P, P, P, P, P, 32768, 896, 896, None, P, None, need, None) == ARG
     assert f(P, P, P, P, P, 64, 100, 64, P, None, None, 0, None) == SHAPE
     assert f(MIS, P, P, P, P, 64, 128, 64, P, None, None, 0, None) == ALIGN
+
+
+def test_packed_codes_check_validation(lib):
+    f = lib.packed_codes_check
+    assert f(None, 4, 64, 3, 4, P, None) == ARG            # codes required
+    assert f(P, 4, 64, 3, 4, None, None) == ARG            # counters required
+    assert f(P, -1, 64, 3, 4, P, None) == ARG
+    assert f(P, 4, 96, 3, 4, P, None) == SHAPE
+    assert f(P, 4, 64, 3, 5, P, None) == UNSUP
+    assert f(P, 4, 64, 9, 8, P, None) == UNSUP
+    assert f(MIS, 4, 64, 3, 4, P, None) == ALIGN
+    assert f(P, 4, 64, 3, 4, P + 4, None) == ALIGN        # int64 counters: 8-byte aligned
+
+
+def test_gemv_desc_layout_matches_header():
+    """The ctypes mirror of sbl_gemv_desc has the header's field order and
+    size (six pointers, two int64, two int32)."""
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct sbl_gemv_desc"):text.index("} sbl_gemv_desc;")]
+    names = re.findall(r"\b([A-Za-z_]+);", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert names == [n for n, _ in sbl.GemvDesc._fields_]
+    assert ctypes.sizeof(sbl.GemvDesc) == 6 * 8 + 2 * 8 + 2 * 4

@@ -49,6 +49,18 @@ def assert_y_close(got, want):
     assert rel.size == 0 or rel.max() <= Y_RTOL, rel.max()
 
 
+def assert_product_full(acc_d, y_d, xq, beta, codes, g, chunk=4096):
+    """Every token of a product against the oracle: acc bit-exact, y within
+    Y_RTOL.  Token chunks bound the host memory of the comparison."""
+    T = xq.shape[0]
+    assert tuple(acc_d.shape) == (T, codes.shape[0]) and tuple(y_d.shape) == (T, codes.shape[0])
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        acc_ref = oracle.gemm_acc(xq[t0:t1], codes)
+        assert np.array_equal(host(acc_d[t0:t1]), acc_ref), f"acc, tokens {t0}..{t1}"
+        assert_y_close(host(y_d[t0:t1]), oracle.dequant(acc_ref, beta[t0:t1], g))
+
+
 def tie_heavy(tag, rows, cols):
     r = synth.rng(tag)
     alphabet = np.array([0.0, -0.0, 0.01, -0.01, 0.02, -0.02, 0.03], dtype=np.float32)
@@ -243,18 +255,14 @@ def test_gemm_extreme_operands(sbl):
                                                 (8292, 896, 4864, False), (16385, 4864, 896, True)])
 def test_gemm_large_tiles(sbl, T, K, N, bf16_scale):
     """Sizes that take the large-tile persistent kernel (at least one tile
-    per CU): ragged token and row edges, K % 128 == 64, N % 4 != 0.  acc and y compared in full on sampled token rows that cover
-    whole tiles at the start and the ragged edge at the end."""
+    per CU): ragged token and row edges, K % 128 == 64, N % 4 != 0; acc and
+    y compared on every token."""
     o = _operands(f"gpu/gemm_big/{T}x{K}x{N}", T, K, N)
     scale = dev(o["gb"]) if bf16_scale else dev(o["g"])
     y, acc = sbl.sparse_bitlinear_gemm(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), scale,
                                        want_acc=True)
-    rnd = synth.rng(f"gpu/gemm_big/{T}x{K}x{N}/rows").choice(T, 64, replace=False)
-    rows = np.unique(np.concatenate([np.arange(300), np.arange(T - 300, T), rnd]))
-    acc_ref = oracle.gemm_acc(o["xq"][rows], o["codes"])
-    assert np.array_equal(host(acc)[rows], acc_ref)
     g_used = oracle.bf16_bits_to_float(o["gb"]) if bf16_scale else o["g"]
-    assert_y_close(host(y)[rows], oracle.dequant(acc_ref, o["beta"][rows], g_used))
+    assert_product_full(acc, y, o["xq"], o["beta"], o["codes"], g_used)
 
 
 @pytest.mark.parametrize("T,K,N", [(16400, 320, 1000), (8193, 896, 896), (300, 896, 200)])
@@ -269,18 +277,17 @@ def test_gemm_stores_stay_in_bounds(sbl, T, K, N):
     y, _ = sbl.sparse_bitlinear_gemm(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), dev(o["g"]), y=y)
     tail = host(ybig[T * N:])
     assert np.isnan(tail).all(), "stores past the end of y"
-    rows = np.unique(np.concatenate([np.arange(min(T, 260)), np.arange(max(0, T - 260), T)]))
-    acc_ref = oracle.gemm_acc(o["xq"][rows], o["codes"])
-    assert_y_close(host(y)[rows], oracle.dequant(acc_ref, o["beta"][rows], o["g"]))
+    acc_ref = oracle.gemm_acc(o["xq"], o["codes"])
+    assert_y_close(host(y), oracle.dequant(acc_ref, o["beta"], o["g"]))
 
 
 @pytest.mark.parametrize("name,N,K", [("q", 896, 896), ("k", 128, 896), ("gate", 4864, 896),
                                       ("down", 896, 4864), ("wide_up", 7168, 2048),
                                       ("wide_down", 2048, 7168)])
-def test_full_size_layer_sampled(sbl, name, N, K):
+def test_full_size_layer(sbl, name, N, K):
     """Full-size prefill shapes (32768 tokens for the 0.5B skeleton, 8192 for
-    the 2048/7168 stack), run end to end on the GPU; weights, codes and
-    scales compared in full, x~ in full, acc and y on 96 sampled tokens."""
+    the 2048/7168 stack), run end to end on the GPU; masks, codes, scales,
+    x~ and beta compared in full, and acc and y on every token."""
     T = 8192 if name.startswith("wide") else 32768
     W = synth.latent_weight(f"cfg/full/{name}/W", N, K)
     x = synth.activations_bf16(f"cfg/full/{name}/x", T, K)
@@ -296,11 +303,7 @@ def test_full_size_layer_sampled(sbl, name, N, K):
     xq, beta = oracle.act_quant(x)
     assert np.array_equal(host(xq_d), xq)
     assert np.array_equal(host(beta_d), beta)
-    rows = np.sort(synth.rng(f"cfg/full/{name}/sample").choice(T, 96, replace=False))
-    rows[-1] = T - 1
-    acc_ref = oracle.gemm_acc(xq[rows], codes)
-    assert np.array_equal(host(acc_d)[rows], acc_ref)
-    assert_y_close(host(y_d)[rows], oracle.dequant(acc_ref, beta[rows], g))
+    assert_product_full(acc_d, y_d, xq, beta, codes, g)
 
 
 def test_full_size_fused_projection_step(sbl):
@@ -308,9 +311,9 @@ def test_full_size_fused_projection_step(sbl):
     the 0.5B skeleton refreshed in one grouped launch into the row ranges of
     four projection buffers (q/k/v, o, gate/up, down), the 4 activation
     inputs quantised, and 4 products at 32768 tokens.  Codes and scales of
-    every linear and x~ / beta compared in full against the oracle, acc and
-    y on 96 sampled tokens; the k and gate column slices equal the products
-    launched on their own."""
+    every linear, x~ / beta, and acc and y of every token compared against
+    the oracle; the k and gate column slices equal the products launched on
+    their own."""
     T = synth.QWEN05B_PREFILL_TOKENS
     dims = {name: (N, K) for name, N, K in synth.QWEN05B_LINEARS}
     groups = (("qkv", ("q", "k", "v"), "attn_in", 896), ("o", ("o",), "attn_out", 896),
@@ -336,10 +339,6 @@ def test_full_size_fused_projection_step(sbl):
         codes[name] = oracle.ternary_codes(w, oracle.nm_mask(w, 3, 4), g)
         assert np.array_equal(host(packed[name]), oracle.pack_codes(codes[name])), name
         assert np.array_equal(host(scale[name]), g), name
-    rows = np.sort(synth.rng("gpu/fused/sample").choice(T, 96, replace=False))
-    rows[-1] = T - 1
-    rows_d = torch.from_numpy(rows).to(DEV)
-    ys = {}
     for gname, members, xn, K in groups:
         x = synth.activations_bf16(f"gpu/fused/{xn}/x", T, K)
         xq_d, beta_d = sbl.act_quant_i8(dev(x))
@@ -350,9 +349,7 @@ def test_full_size_fused_projection_step(sbl):
                                                want_acc=True)
         c = np.concatenate([codes[mn] for mn in members])
         g = host(scale_f[gname])
-        acc_ref = oracle.gemm_acc(xq[rows], c)
-        assert np.array_equal(host(acc_d[rows_d]), acc_ref), gname
-        assert_y_close(host(y_d[rows_d]), oracle.dequant(acc_ref, beta[rows], g))
+        assert_product_full(acc_d, y_d, xq, beta, c, g)
         for mn in members:
             if mn in ("k", "gate"):
                 r0 = sum(dims[o][0] for o in members[:members.index(mn)])
@@ -381,11 +378,11 @@ def test_sparse24_matches_dense(sbl, T, K, N):
 
 @pytest.mark.parametrize("name,N,K", [("q", 896, 896), ("gate", 4864, 896), ("down", 896, 4864),
                                       ("qkv", 1152, 896), ("gate_up", 9728, 896)])
-def test_sparse24_full_size_sampled(sbl, name, N, K):
+def test_sparse24_full_size(sbl, name, N, K):
     """The 2:4 product at the 0.5B skeleton's prefill size (32768 tokens),
     per linear and on the fused projections the benchmark times: acc and y
-    on 96 sampled tokens against the oracle, and y equal to the dense
-    product's everywhere."""
+    of every token against the oracle, and y equal to the dense product's
+    everywhere."""
     T = synth.QWEN05B_PREFILL_TOKENS
     W = synth.latent_weight(f"gpu/sp24full/{name}/W", N, K)
     x = synth.activations_bf16(f"gpu/sp24full/{name}/x", T, K)
@@ -400,12 +397,7 @@ def test_sparse24_full_size_sampled(sbl, name, N, K):
     yd = sbl.sparse_bitlinear_gemm(dev(xq), dev(beta), packed, dev(g))[0]
     assert int(bad.item()) == 0
     assert torch.equal(y, yd)
-    rows = np.sort(synth.rng(f"gpu/sp24full/{name}/sample").choice(T, 96, replace=False))
-    rows[-1] = T - 1
-    acc_ref = oracle.gemm_acc(xq[rows], codes)
-    rows_d = torch.from_numpy(rows).to(DEV)
-    assert np.array_equal(host(acc[rows_d]), acc_ref)
-    assert_y_close(host(y[rows_d]), oracle.dequant(acc_ref, beta[rows], g))
+    assert_product_full(acc, y, xq, beta, codes, g)
 
 
 @pytest.mark.parametrize("T,K,N,bf16_scale", [(16400, 320, 1000, False), (16400, 192, 1004, True),
@@ -415,8 +407,8 @@ def test_sparse24_large_tiles(sbl, T, K, N, bf16_scale):
     """Sizes that take the large-tile smfmac kernel (at least one 256 x 256
     tile per CU, N % 4 == 0): ragged token and row edges, K % 128 == 64,
     bf16 row scales; N % 4 != 0 takes the small-tile kernel.  y equal to the
-    dense product's everywhere; acc and y against the oracle on token rows
-    that cover whole tiles at both ends."""
+    dense product's everywhere; acc and y of every token against the
+    oracle."""
     o = _operands(f"gpu/sp24_big/{T}x{K}x{N}", T, K, N, n=2, m=4)
     scale = dev(o["gb"]) if bf16_scale else dev(o["g"])
     bad = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -426,12 +418,8 @@ def test_sparse24_large_tiles(sbl, T, K, N, bf16_scale):
     yd = sbl.sparse_bitlinear_gemm(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), scale)[0]
     assert int(bad.item()) == 0
     assert torch.equal(y, yd)
-    rnd = synth.rng(f"gpu/sp24_big/{T}x{K}x{N}/rows").choice(T, 64, replace=False)
-    rows = np.unique(np.concatenate([np.arange(300), np.arange(T - 300, T), rnd]))
-    acc_ref = oracle.gemm_acc(o["xq"][rows], o["codes"])
-    assert np.array_equal(host(acc)[rows], acc_ref)
     g_used = oracle.bf16_bits_to_float(o["gb"]) if bf16_scale else o["g"]
-    assert_y_close(host(y)[rows], oracle.dequant(acc_ref, o["beta"][rows], g_used))
+    assert_product_full(acc, y, o["xq"], o["beta"], o["codes"], g_used)
 
 
 def test_sparse24_stores_stay_in_bounds(sbl):
@@ -453,10 +441,7 @@ def test_sparse24_stores_stay_in_bounds(sbl):
     torch.cuda.synchronize()
     assert np.isnan(host(ybig[T * N:])).all(), "stores past the end of y"
     assert (host(abig[T * N:]) == -7).all(), "stores past the end of acc"
-    rows = np.unique(np.concatenate([np.arange(260), np.arange(T - 260, T)]))
-    acc_ref = oracle.gemm_acc(o["xq"][rows], o["codes"])
-    assert np.array_equal(host(acc)[rows], acc_ref)
-    assert_y_close(host(y)[rows], oracle.dequant(acc_ref, o["beta"][rows], o["g"]))
+    assert_product_full(acc, y, o["xq"], o["beta"], o["codes"], o["g"])
 
 
 def test_sparse24_counts_groups_that_are_not_2of4(sbl):
@@ -468,17 +453,49 @@ def test_sparse24_counts_groups_that_are_not_2of4(sbl):
 
 
 # ---------------------------------------------------------------- decode
-@pytest.mark.parametrize("T", [1, 4, 16, 3])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 16])
 @pytest.mark.parametrize("N,K", [(512, 256), (896, 896), (128, 896), (4864, 896), (896, 4864),
-                                 (100, 192), (2048, 7168)])
-def test_gemv(sbl, T, N, K):
+                                 (100, 192), (2048, 7168), (33, 64), (31, 576)])
+@pytest.mark.parametrize("bf16_scale", [True, False])
+def test_gemv(sbl, T, N, K, bf16_scale):
+    """The decode product on every kernel it has: vector ALU for 1, 2 and up
+    to 4 tokens, matrix cores above; acc bit-exact and y within Y_RTOL on
+    every output (row counts not a multiple of the 32-row unit, K not a
+    multiple of the 512-code step)."""
     o = _operands(f"gpu/gemv/{N}x{K}", T, K, N)
-    y = sbl.sparse_bitlinear_gemv(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), dev(o["gb"]))
+    scale = dev(o["gb"]) if bf16_scale else dev(o["g"])
+    y, acc = sbl.sparse_bitlinear_gemv(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), scale,
+                                       want_acc=True)
     acc_ref = oracle.gemm_acc(o["xq"], o["codes"])
+    assert np.array_equal(host(acc), acc_ref)
+    g = oracle.bf16_bits_to_float(o["gb"]) if bf16_scale else o["g"]
+    assert_y_close(host(y), oracle.dequant(acc_ref, o["beta"], g))
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 16])
+def test_gemv_stores_stay_in_bounds(sbl, T):
+    """y and acc of the decode product sit inside larger buffers filled with
+    a sentinel: nothing past T x N is written (N = 1000 is not a multiple
+    of the 32- or 64-row unit)."""
+    N, K = 1000, 896
+    o = _operands("gpu/gemv_guard", T, K, N)
+    ybig = torch.full((T * N + 256,), float("nan"), dtype=torch.float32, device=DEV)
+    abig = torch.full((T * N + 256,), -7, dtype=torch.int32, device=DEV)
+    xq, beta, packed, g = dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), dev(o["gb"])
+    y, acc = ybig[:T * N].view(T, N), abig[:T * N].view(T, N)
+    st = sbl.load().sparse_bitlinear_gemv(
+        sbl._ptr(xq), sbl._ptr(beta), sbl._ptr(packed), sbl._ptr(g), sbl.SCALE_BF16, T, K, N,
+        sbl._ptr(y), sbl._ptr(acc), sbl._stream(xq.device))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert np.isnan(host(ybig[T * N:])).all(), "stores past the end of y"
+    assert (host(abig[T * N:]) == -7).all(), "stores past the end of acc"
+    acc_ref = oracle.gemm_acc(o["xq"], o["codes"])
+    assert np.array_equal(host(acc), acc_ref)
     assert_y_close(host(y), oracle.dequant(acc_ref, o["beta"], oracle.bf16_bits_to_float(o["gb"])))
 
 
-@pytest.mark.parametrize("T", [1, 16])
+@pytest.mark.parametrize("T", [1, 2, 4, 16])
 def test_gemv_grouped(sbl, T):
     shapes = [("q", 896, 896), ("k", 128, 896), ("v", 128, 896), ("o", 896, 896),
               ("gate", 4864, 896), ("up", 4864, 896), ("down", 896, 4864), ("tiny", 36, 64)]
@@ -487,7 +504,9 @@ def test_gemv_grouped(sbl, T):
         o = _operands(f"gpu/gemvg/{name}", T, K, N, n=2 if name == "o" else 3)
         jobs.append(dict(xq=dev(o["xq"]), beta=dev(o["beta"]), packed=dev(o["packed"]),
                          scale=dev(o["gb"]) if name != "v" else dev(o["g"]),
-                         y=torch.full((T, N), float("nan"), device=DEV)))
+                         y=torch.full((T, N), float("nan"), device=DEV),
+                         acc=torch.full((T, N), -7, dtype=torch.int32, device=DEV)
+                         if name != "k" else None))
         refs.append(o)
     hostd, devd = sbl.gemv_descs(jobs)
     sbl.sparse_bitlinear_gemv_grouped(hostd, devd, len(jobs), T, DEV)
@@ -495,14 +514,17 @@ def test_gemv_grouped(sbl, T):
     for (name, N, K), j, o in zip(shapes, jobs, refs):
         g = o["g"] if name == "v" else oracle.bf16_bits_to_float(o["gb"])
         acc_ref = oracle.gemm_acc(o["xq"], o["codes"])
+        if j["acc"] is not None:
+            assert np.array_equal(host(j["acc"]), acc_ref), name
         assert_y_close(host(j["y"]), oracle.dequant(acc_ref, o["beta"], g))
 
 
-@pytest.mark.parametrize("T,n", [(1, 3), (16, 3), (1, 2)])
+@pytest.mark.parametrize("T,n", [(1, 3), (4, 3), (16, 3), (1, 2)])
 def test_gemv_grouped_full_sweep(sbl, T, n):
     """The decode sweep as the benchmark launches it: all 168 linears of the
     0.5B skeleton (24 layers x 7) in one grouped call, bf16 row scales, one
-    x~ per input width, at 3:4 and at 2:4; every output against the oracle."""
+    x~ per input width, at 3:4 and at 2:4; every int32 accumulator
+    (bit-exact) and every y against the oracle."""
     K_in = {"q": 896, "k": 896, "v": 896, "o": 896, "gate": 896, "up": 896, "down": 4864}
     xs = {}
     for K in (896, 4864):
@@ -516,14 +538,99 @@ def test_gemv_grouped_full_sweep(sbl, T, n):
             g, gb = oracle.row_scale(W)
             codes = oracle.ternary_codes(W, oracle.nm_mask(W, n, 4), g)
             jobs.append(dict(xq=xd[K][0], beta=xd[K][1], packed=dev(oracle.pack_codes(codes)),
-                             scale=dev(gb), y=torch.full((T, N), float("nan"), device=DEV)))
+                             scale=dev(gb), y=torch.full((T, N), float("nan"), device=DEV),
+                             acc=torch.full((T, N), -7, dtype=torch.int32, device=DEV)))
             refs.append((codes, oracle.bf16_bits_to_float(gb), K))
     hostd, devd = sbl.gemv_descs(jobs)
     sbl.sparse_bitlinear_gemv_grouped(hostd, devd, len(jobs), T, DEV)
     torch.cuda.synchronize()
     for j, (codes, g, K) in zip(jobs, refs):
         xq, beta = xs[K]
-        assert_y_close(host(j["y"]), oracle.dequant(oracle.gemm_acc(xq, codes), beta, g))
+        acc_ref = oracle.gemm_acc(xq, codes)
+        assert np.array_equal(host(j["acc"]), acc_ref)
+        assert_y_close(host(j["y"]), oracle.dequant(acc_ref, beta, g))
+
+
+# ------------------------------------------------- stray 11 fields, validator
+def _with_stray_fields(packed, tag, frac=0.1):
+    """The packed codes with a seeded share of their zero fields (00) set to
+    the non-code 11 (model card "Packed vs raw" lists 00, 01, 10 only):
+    every decoder reads 11 as 0, so products and their accumulators must
+    not change."""
+    rng = synth.rng(tag)
+    p = packed.copy()
+    for r in range(4):
+        f = (p >> (2 * r)) & 3
+        hit = (f == 0) & (rng.random(p.shape) < frac)
+        p[hit] |= np.uint8(3 << (2 * r))
+    return p
+
+
+@pytest.mark.parametrize("T,K,N", [(300, 896, 200), (8192, 896, 2048), (33, 64, 4)])
+def test_stray_fields_read_as_zero_gemm(sbl, T, K, N):
+    """Small-tile and large-tile (at least one 256 x 256 tile per CU)
+    prefill kernels on codes carrying stray 11 fields."""
+    o = _operands(f"gpu/stray/gemm/{T}x{K}x{N}", T, K, N)
+    dirty = _with_stray_fields(o["packed"], f"gpu/stray/gemm/{T}x{K}x{N}/f")
+    assert ((dirty >> 6) == 3).any() or ((dirty & 3) == 3).any()
+    assert np.array_equal(oracle.unpack_codes(dirty, K), o["codes"])
+    y, acc = sbl.sparse_bitlinear_gemm(dev(o["xq"]), dev(o["beta"]), dev(dirty), dev(o["g"]),
+                                       want_acc=True)
+    assert_product_full(acc, y, o["xq"], o["beta"], oracle.unpack_codes(dirty, K), o["g"])
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 16])
+def test_stray_fields_read_as_zero_gemv(sbl, T):
+    N, K = 896, 4864
+    o = _operands("gpu/stray/gemv", T, K, N)
+    dirty = _with_stray_fields(o["packed"], "gpu/stray/gemv/f")
+    y, acc = sbl.sparse_bitlinear_gemv(dev(o["xq"]), dev(o["beta"]), dev(dirty), dev(o["gb"]),
+                                       want_acc=True)
+    acc_ref = oracle.gemm_acc(o["xq"], oracle.unpack_codes(dirty, K))
+    assert np.array_equal(host(acc), acc_ref)
+    assert_y_close(host(y), oracle.dequant(acc_ref, o["beta"], oracle.bf16_bits_to_float(o["gb"])))
+
+
+@pytest.mark.parametrize("T,K,N", [(300, 896, 200), (8192, 896, 2048)])
+def test_stray_fields_read_as_zero_sparse24(sbl, T, K, N):
+    """2:4 codes whose zero slots carry stray 11 fields: the compressor
+    counts no bad group and the smfmac product equals the oracle's."""
+    o = _operands(f"gpu/stray/sp24/{T}x{K}x{N}", T, K, N, n=2, m=4)
+    dirty = _with_stray_fields(o["packed"], f"gpu/stray/sp24/{T}x{K}x{N}/f")
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    img = sbl.sparse24_compress(dev(dirty), bad)
+    y, acc = sbl.sparse_bitlinear_gemm_sparse24(dev(o["xq"]), dev(o["beta"]), img, N, dev(o["g"]),
+                                                want_acc=True)
+    assert int(bad.item()) == 0
+    assert_product_full(acc, y, o["xq"], o["beta"], oracle.unpack_codes(dirty, K), o["g"])
+
+
+@pytest.mark.parametrize("n,m", [(3, 4), (2, 4), (1, 4), (6, 8), (4, 8), (0, 4), (8, 8)])
+@pytest.mark.parametrize("rows,cols", [(1, 64), (37, 896), (300, 4864)])
+def test_packed_codes_check(sbl, n, m, rows, cols):
+    """The validator against the oracle on clean codes (an n:m mask) and on
+    codes with stray 11 fields and over-full groups planted."""
+    W = synth.latent_weight(f"gpu/pcheck/{rows}x{cols}", rows, cols)
+    mask = oracle.nm_mask(W, max(n, 1) if n < m else m, m)
+    g, _ = oracle.row_scale(W)
+    packed = oracle.pack_codes(oracle.ternary_codes(W, mask, g))
+    dirty = _with_stray_fields(packed, f"gpu/pcheck/{rows}x{cols}/f", 0.02)
+    rng = synth.rng(f"gpu/pcheck/{rows}x{cols}/full")
+    full = rng.random(dirty.shape) < 0.01
+    dirty[full] = 0x55                      # four +1 codes: a full group of 4
+    for arr in (packed, dirty):
+        st = host(sbl.packed_codes_check(dev(arr), n, m))
+        assert tuple(st.tolist()) == oracle.packed_check(arr, cols, n, m)
+
+
+def test_packed_codes_check_of_the_full_layer(sbl):
+    """The codes the grouped refresh writes for a 0.5B-skeleton layer (3:4)
+    validate clean: no 11 field, no group of 4 with more than 3 nonzeros."""
+    for name, N, K in synth.QWEN05B_LINEARS:
+        W = dev(synth.latent_weight(f"gpu/pcheck/layer/{name}", N, K))
+        _, packed, _, _ = sbl.nm_mask_quant_pack(W, 3, 4)
+        assert host(sbl.packed_codes_check(packed, 3, 4)).tolist() == [0, 0], name
+        assert host(sbl.packed_codes_check(packed, 2, 4))[1] > 0, name
 
 
 # ------------------------------------------------------------- plumbing
@@ -568,6 +675,23 @@ def test_binding_rejects_mis_sized_buffers(sbl):
     with pytest.raises(ValueError):
         sbl.act_quant_i8(torch.zeros((4, 64), dtype=torch.int16, device=DEV),
                          torch.empty((4, 63), dtype=torch.int8, device=DEV))
+    p24 = torch.zeros((8, 64), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):       # image smaller than sparse24_bytes
+        sbl.sparse24_compress(p24, out=torch.empty(8 * 256 // 4 - 16, dtype=torch.uint8, device=DEV))
+    with pytest.raises(ValueError):       # image on the host
+        sbl.sparse24_compress(p24, out=torch.empty(8 * 256 // 4, dtype=torch.uint8))
+    with pytest.raises(TypeError):        # image of another dtype
+        sbl.sparse24_compress(p24, out=torch.empty(8 * 256 // 16, dtype=torch.int32, device=DEV))
+    with pytest.raises(TypeError):        # counter of another dtype
+        sbl.sparse24_compress(p24, torch.zeros(1, dtype=torch.int64, device=DEV))
+    with pytest.raises(ValueError):       # counter on the host
+        sbl.sparse24_compress(p24, torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError):       # no counter element
+        sbl.sparse24_compress(p24, torch.zeros(0, dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError):       # GEMV accumulators of the wrong shape
+        sbl.gemv_descs([dict(xq=xq[:2].contiguous(), beta=ok["beta"][:2].contiguous(), packed=packed,
+                             scale=ok["scale"], y=torch.empty((2, 8), device=DEV),
+                             acc=torch.empty((2, 7), dtype=torch.int32, device=DEV))])
 
 
 def test_repeat_runs_are_bitwise_identical(sbl):

@@ -87,3 +87,60 @@ def test_packed_size_matches_model_card():
     assert round(packed / MiB) == s["packed_MB"]
     # the raw pickle carries some framing beyond the tensor bytes (942.2 MiB)
     assert s["state_dict_bf16_MB"] - 1 < raw / MiB <= s["state_dict_bf16_MB"]
+
+
+# ------------------------------------------------------- packed-code validator
+def _brute_check(packed, cols, n, m):
+    """Field-by-field count in plain Python: fields 11, and m-groups with
+    more than n fields 01 / 10."""
+    not_code = over_n = 0
+    for row in packed.tolist():
+        fields = [(byte >> (2 * r)) & 3 for byte in row for r in range(4)]
+        assert len(fields) == cols
+        for g in range(0, cols, m):
+            grp = fields[g:g + m]
+            not_code += sum(1 for f in grp if f == 3)
+            over_n += sum(1 for f in grp if f in (1, 2)) > n
+    return not_code, over_n
+
+
+def test_packed_check_hand_decoded_byte():
+    # 0xE4 = 11 10 01 00: columns 0..3 hold 0, +1, -1 and the non-code 11
+    packed = np.full((1, 16), 0x00, np.uint8)
+    packed[0, 0] = 0xE4
+    assert oracle.packed_check(packed, 64, 1, 4) == (1, 1)
+    assert oracle.packed_check(packed, 64, 2, 4) == (1, 0)
+    # an 8-group spanning bytes 0 and 1: 2 nonzeros from 0xE4, 4 from 0x55
+    packed[0, 1] = 0x55
+    assert oracle.packed_check(packed, 64, 5, 8) == (1, 1)
+    assert oracle.packed_check(packed, 64, 6, 8) == (1, 0)
+
+
+def test_packed_check_against_brute_force():
+    rng = np.random.default_rng(11)
+    packed = rng.integers(0, 256, size=(7, 48), dtype=np.uint8)   # every field value
+    packed[0] = np.arange(48, dtype=np.uint8)                     # bytes 0..47
+    packed[1] = np.arange(208, 256, dtype=np.uint8)                # bytes 208..255
+    for m in (4, 8):
+        for n in range(m + 1):
+            assert oracle.packed_check(packed, 192, n, m) == _brute_check(packed, 192, n, m), (n, m)
+
+
+def test_packed_check_clean_for_masked_codes():
+    from sparse_linear_layers_amd import synth
+    for n, m in [(3, 4), (2, 4), (1, 4), (6, 8), (4, 8)]:
+        W = synth.latent_weight(f"test/pcheck/{n}{m}", 33, 256)
+        mask = oracle.nm_mask(W, n, m)
+        g, _ = oracle.row_scale(W)
+        codes = oracle.ternary_codes(W, mask, g)
+        packed = oracle.pack_codes(codes)
+        assert oracle.packed_check(packed, 256, n, m) == (0, 0)
+        # with a smaller n the count is the groups holding more nonzeros
+        nz = (codes.reshape(33, -1, m) != 0).sum(-1)
+        assert oracle.packed_check(packed, 256, n - 1, m)[1] == int((nz > n - 1).sum())
+        # planted 11 fields: each is counted once and reads as no nonzero
+        bad = packed.copy()
+        bad[5, 3] |= 0x3 << 2
+        bad[17, 60] |= 0x3 << 6
+        got = oracle.packed_check(bad, 256, n, m)
+        assert got[0] == 2 and got[1] == 0
