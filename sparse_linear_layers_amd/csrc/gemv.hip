@@ -574,12 +574,9 @@ hipError_t launch_gemv(const sbl_gemv_desc* host, const sbl_gemv_desc* dev, int 
     a.block_start[n] = (int)units;
     if (units > 0) {
       hipError_t e;
-      if (T == 1) {
-        e = launch_valu<1>(a, units, stream);
-      } else if (T == 2) {
-        e = launch_valu<2>(a, units, stream);
-      } else if (T <= kGemvValuMaxTokens) {
-        e = launch_valu<4>(a, units, stream);
+      if (T <= kGemvValuMaxTokens) {
+        e = T == 1 ? launch_valu<1>(a, units, stream)
+                   : T == 2 ? launch_valu<2>(a, units, stream) : launch_valu<4>(a, units, stream);
       } else {
         static std::atomic<int> cache[kMaxDevices];
         const int grid = (int)std::min<int64_t>(units, (int64_t)resident_slots(gemv_kernel<4>, cache, stream));
