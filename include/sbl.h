@@ -72,6 +72,7 @@ extern "C" {
 #define SBL_ERR_ALIGN (-3)       /* a base pointer is not 16-byte aligned              */
 #define SBL_ERR_UNSUPPORTED (-4) /* (n, m) or option outside what is implemented       */
 #define SBL_ERR_HIP (-5)         /* the HIP runtime reported an error at launch        */
+#define SBL_ERR_TOO_LARGE (-6)   /* needs more than the library's fixed scratch holds  */
 
 /* Largest cols (K) accepted: keeps |acc| <= 127*K well inside int32 and the
  * per-row work of the weight kernels bounded. */
@@ -338,6 +339,29 @@ int sparse_bitlinear_ste_backward(const float* dy, const int8_t* xq, const float
                                   const uint8_t* packed, const float* row_scale, int64_t T,
                                   int64_t K, int64_t N, float* dx, float* dw, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving or training loops, harnesses
+ * that forbid hipMalloc).  Same contract and the same results, bit for bit,
+ * as sparse_bitlinear_ste_backward, without a workspace argument: the
+ * workspace is a device array owned by the library, SBL_STE_SCRATCH_BYTES
+ * per GPU, which comes with the library's code object and is held until the
+ * process ends.  The call itself allocates nothing.
+ * Every call on one GPU uses that GPU's array: calls that overlap on one GPU
+ * (different streams) race.  The array keeps the last call's contents; a
+ * call writes every byte of it that it reads.
+ * Errors: as sparse_bitlinear_ste_backward; SBL_ERR_TOO_LARGE when dw is
+ * requested and sparse_bitlinear_ste_workspace_bytes(T, K, N) exceeds
+ * SBL_STE_SCRATCH_BYTES (the 0.5B skeleton's linears at 32768 tokens need
+ * at most 53 MB); SBL_ERR_HIP when the array's device address cannot be
+ * obtained.
+ * ------------------------------------------------------------------------ */
+#define SBL_STE_SCRATCH_BYTES ((size_t)64 << 20)
+int sparse_bitlinear_ste_backward_noalloc(const float* dy, const int8_t* xq, const float* beta,
+                                          const uint8_t* packed, const float* row_scale,
+                                          int64_t T, int64_t K, int64_t N, float* dx, float* dw,
+                                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

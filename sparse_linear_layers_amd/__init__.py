@@ -29,7 +29,8 @@ __all__ = [
     "sparse_bitlinear_gemv_grouped", "GemvDesc", "RefreshDesc", "refresh_descs", "gemv_descs",
     "SCALE_FROM_MASKED", "SCALE_PER_TENSOR", "SCALE_F32", "SCALE_BF16", "GEMV_MAX_TOKENS",
     "rmsnorm_act_quant_i8", "nm_mask_stats", "packed_codes_check", "sparse_bitlinear_ste_backward",
-    "sparse_bitlinear_ste_workspace_bytes",
+    "sparse_bitlinear_ste_workspace_bytes", "sparse_bitlinear_ste_backward_noalloc",
+    "STE_SCRATCH_BYTES",
 ]
 
 SCALE_FROM_MASKED = 1
@@ -38,6 +39,7 @@ SCALE_F32 = 0
 SCALE_BF16 = 1
 GEMV_MAX_TOKENS = 16
 GEMV_MAX_ROWS = 1 << 28
+STE_SCRATCH_BYTES = 64 << 20  # library-owned workspace of the allocation-free backward
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libsbl.so")
@@ -90,6 +92,7 @@ def load() -> ctypes.CDLL:
         "packed_codes_check": [P, I64, I64, I, I, P, P],
         "sparse_bitlinear_ste_backward": [P, P, P, P, P, I64, I64, I64, P, P, P,
                                           ctypes.c_size_t, P],
+        "sparse_bitlinear_ste_backward_noalloc": [P, P, P, P, P, I64, I64, I64, P, P, P],
         "sparse_bitlinear_gemm": [P, P, P, P, I, I64, I64, I64, P, P, P],
         "sparse24_compress": [P, I64, I64, P, P, P],
         "sparse_bitlinear_gemm_sparse24": [P, P, P, P, I, I64, I64, I64, P, P, P],
@@ -325,6 +328,33 @@ def sparse_bitlinear_ste_backward(dy, xq, beta, packed, scale, want_dx: bool = T
     _check("sparse_bitlinear_ste_backward", load().sparse_bitlinear_ste_backward(
         _ptr(dy), _ptr(xq), _ptr(beta), _ptr(packed), _ptr(scale), T, K, N, _ptr(dx), _ptr(dw),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)))
+    return dx, dw
+
+
+def sparse_bitlinear_ste_backward_noalloc(dy, xq, beta, packed, scale,
+                                          dx: torch.Tensor | None = None,
+                                          dw: torch.Tensor | None = None):
+    """The straight-through backward through the allocation-free entry
+    point: the library computes in its own fixed device workspace, and the
+    outputs are the caller's (dx float32 [T, K], dw float32 [N, K]; at least
+    one of them).  Returns (dx, dw)."""
+    _need(dy, torch.float32, "dy", 2)
+    _need(xq, torch.int8, "xq", 2)
+    T, N = dy.shape
+    K = xq.shape[1]
+    _shape(xq, (T, K), torch.int8, "xq")
+    _shape(beta, (T,), torch.float32, "beta")
+    _shape(packed, (N, K // 4), torch.uint8, "packed")
+    _shape(scale, (N,), torch.float32, "scale")
+    if dx is None and dw is None:
+        raise ValueError("dx, dw: pass at least one output")
+    if dx is not None:
+        _shape(dx, (T, K), torch.float32, "dx")
+    if dw is not None:
+        _shape(dw, (N, K), torch.float32, "dw")
+    _check("sparse_bitlinear_ste_backward_noalloc", load().sparse_bitlinear_ste_backward_noalloc(
+        _ptr(dy), _ptr(xq), _ptr(beta), _ptr(packed), _ptr(scale), T, K, N, _ptr(dx), _ptr(dw),
+        _stream(dy.device)))
     return dx, dw
 
 

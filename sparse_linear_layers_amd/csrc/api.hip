@@ -40,6 +40,7 @@ const char* sbl_status_str(int status) {
     case SBL_ERR_ALIGN: return "pointer not 16-byte aligned";
     case SBL_ERR_UNSUPPORTED: return "unsupported option (n, m, flags, scale dtype or token count)";
     case SBL_ERR_HIP: return "HIP runtime error at launch";
+    case SBL_ERR_TOO_LARGE: return "problem needs more than the library's fixed scratch (SBL_STE_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -255,27 +256,61 @@ size_t sparse_bitlinear_ste_workspace_bytes(int64_t T, int64_t K, int64_t N) {
   return sbl::ste_workspace_bytes(T, K, N);
 }
 
-int sparse_bitlinear_ste_backward(const float* dy, const int8_t* xq, const float* beta,
-                                  const uint8_t* packed, const float* row_scale, int64_t T,
-                                  int64_t K, int64_t N, float* dx, float* dw, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
+// Checks of the backward's arguments other than its workspace; on success
+// *dx_out / *dw_out are the outputs to compute (NULL when empty) and *need
+// the workspace bytes.
+static int check_ste(const float* dy, const int8_t* xq, const float* beta, const uint8_t* packed,
+                     const float* row_scale, int64_t T, int64_t K, int64_t N, float** dx_out,
+                     float** dw_out, size_t* need) {
   if (T < 0 || N < 0 || T > kMaxRows || N > kMaxRows) return SBL_ERR_ARG;
   if (int s = check_cols(K)) return s;
   if (N > (int64_t(1) << 22)) return SBL_ERR_SHAPE;  // 32-bit per-lane offsets into dy tiles
-  if (T == 0) dx = nullptr;  // empty outputs
-  if (N == 0) dw = nullptr;
+  float* dx = T == 0 ? nullptr : *dx_out;            // empty outputs
+  float* dw = N == 0 ? nullptr : *dw_out;
+  *dx_out = dx;
+  *dw_out = dw;
+  *need = 0;
   if (!dx && !dw) return SBL_OK;
   const bool reads = T > 0 && N > 0;  // otherwise the reduction is empty: zeros
   if (reads && !dy) return SBL_ERR_ARG;
   if (N > 0 && !row_scale) return SBL_ERR_ARG;
   if (dx && reads && !packed) return SBL_ERR_ARG;
   if (dw && reads && (!xq || !beta)) return SBL_ERR_ARG;
-  const size_t need = dw ? sbl::ste_workspace_bytes(T, K, N) : 0;
-  if (need > 0 && (!workspace || workspace_bytes < need)) return SBL_ERR_ARG;
   if (!aligned16_or_null(dy) || !aligned16_or_null(row_scale) || !aligned16_or_null(xq) ||
       !aligned16_or_null(beta) || !aligned16_or_null(packed) || !aligned16_or_null(dx) ||
-      !aligned16_or_null(dw) || (need > 0 && !aligned16(workspace)))
+      !aligned16_or_null(dw))
     return SBL_ERR_ALIGN;
+  *need = dw ? sbl::ste_workspace_bytes(T, K, N) : 0;
+  return SBL_OK;
+}
+
+int sparse_bitlinear_ste_backward_noalloc(const float* dy, const int8_t* xq, const float* beta,
+                                          const uint8_t* packed, const float* row_scale,
+                                          int64_t T, int64_t K, int64_t N, float* dx, float* dw,
+                                          hipStream_t stream) {
+  size_t need = 0;
+  if (int s = check_ste(dy, xq, beta, packed, row_scale, T, K, N, &dx, &dw, &need)) return s;
+  if (!dx && !dw) return SBL_OK;
+  if (need > SBL_STE_SCRATCH_BYTES) return SBL_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (need > 0 && sbl::ste_scratch(sbl::stream_device(stream), &ws) != hipSuccess) {
+    (void)hipGetLastError();
+    return SBL_ERR_HIP;
+  }
+  (void)hipGetLastError();
+  return hip_status(sbl::launch_ste_backward(dy, xq, beta, packed, row_scale, T, K, N, dx, dw, ws,
+                                             stream));
+}
+
+int sparse_bitlinear_ste_backward(const float* dy, const int8_t* xq, const float* beta,
+                                  const uint8_t* packed, const float* row_scale, int64_t T,
+                                  int64_t K, int64_t N, float* dx, float* dw, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  if (int s = check_ste(dy, xq, beta, packed, row_scale, T, K, N, &dx, &dw, &need)) return s;
+  if (!dx && !dw) return SBL_OK;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SBL_ERR_ARG;
+  if (need > 0 && !aligned16(workspace)) return SBL_ERR_ALIGN;
   (void)hipGetLastError();
   return hip_status(sbl::launch_ste_backward(dy, xq, beta, packed, row_scale, T, K, N, dx, dw,
                                              need > 0 ? workspace : nullptr, stream));

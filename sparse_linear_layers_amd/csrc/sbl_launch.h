@@ -99,6 +99,9 @@ hipError_t launch_gemm_sparse24(const int8_t* xq, const float* beta, const void*
                                 const void* scale, int scale_bf16, int64_t T, int64_t K, int64_t N,
                                 float* y, int32_t* acc, hipStream_t stream);
 size_t ste_workspace_bytes(int64_t T, int64_t K, int64_t N);
+// Device address of the library's SBL_STE_SCRATCH_BYTES workspace on device
+// `dev` (set up on the first call for that device).
+hipError_t ste_scratch(int dev, void** out);
 hipError_t launch_ste_backward(const float* dy, const int8_t* xq, const float* beta,
                                const uint8_t* packed, const float* gamma, int64_t T, int64_t K,
                                int64_t N, float* dx, float* dw, void* workspace,

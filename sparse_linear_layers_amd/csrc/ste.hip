@@ -373,6 +373,40 @@ __global__ __launch_bounds__(256) void ste_token_scale_kernel(const float* __res
   if (t < T) out[t] = beta[t] / 127.0f;
 }
 
+// ---------------------------------------------------------------------------
+// Workspace of the allocation-free entry point: a device array that comes
+// with the code object (each GPU the library runs on holds its own copy
+// until the process ends).  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels get the address that
+// hipGetSymbolAddress reports for the device the work runs on, queried once
+// per device with that device current.
+static __device__ __align__(256) uint8_t scratch[SBL_STE_SCRATCH_BYTES];
+
+static std::atomic<uintptr_t> scratch_addr[kMaxDevices];
+
+hipError_t ste_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uintptr_t v = scratch_addr[dev].load(std::memory_order_acquire);
+  if (v == 0) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    v = reinterpret_cast<uintptr_t>(p);
+    scratch_addr[dev].store(v, std::memory_order_release);  // concurrent first calls store the same value
+  }
+  *out = reinterpret_cast<void*>(v);
+  return hipSuccess;
+}
+
 hipError_t launch_ste_backward(const float* dy, const int8_t* xq, const float* beta,
                                const uint8_t* packed, const float* gamma, int64_t T, int64_t K,
                                int64_t N, float* dx, float* dw, void* workspace,

@@ -210,3 +210,21 @@ def test_gemv_desc_layout_matches_header():
     names = re.findall(r"\b([A-Za-z_]+);", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
     assert names == [n for n, _ in sbl.GemvDesc._fields_]
     assert ctypes.sizeof(sbl.GemvDesc) == 6 * 8 + 2 * 8 + 2 * 4
+
+
+def test_ste_backward_noalloc_validation(lib):
+    f = lib.sparse_bitlinear_ste_backward_noalloc
+    wsb = lib.sparse_bitlinear_ste_workspace_bytes
+    wsb.argtypes = [ctypes.c_int64] * 3
+    wsb.restype = ctypes.c_size_t
+    assert f(P, P, P, P, P, 64, 128, 64, None, None, None) == OK          # nothing requested
+    assert f(P, P, P, P, P, 0, 128, 64, P, None, None) == OK              # empty dx
+    assert f(None, P, P, P, P, 64, 128, 64, P, None, None) == ARG
+    assert f(P, P, P, None, P, 64, 128, 64, P, None, None) == ARG         # dx needs codes
+    assert f(P, P, P, P, P, 64, 100, 64, P, None, None) == SHAPE
+    assert f(MIS, P, P, P, P, 64, 128, 64, P, None, None) == ALIGN
+    # a dw whose workspace exceeds the fixed scratch is refused before any launch
+    big = (1 << 25, 128, 64)                 # beta/127 alone is 128 MiB
+    assert wsb(*big) > sbl.STE_SCRATCH_BYTES
+    assert f(P, P, P, P, P, *big, None, P, None) == -6
+    assert lib.sbl_status_str(-6)
