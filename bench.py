@@ -46,6 +46,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PEAK_I8_TOPS = 5000.0      # MI355X dense int8 matrix peak (5.0 POP/s)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (2.5 PFLOP/s)
+# ops per HBM byte above which the int8 matrix cores, not HBM, bound a kernel
+RIDGE_OPS_PER_BYTE = PEAK_I8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+FLUSH_BYTES = 512 << 20    # twice the 256 MB Infinity Cache
 METRIC = "Sparse-BitLinear int8 TOPS (prefill) + HBM GB/s (decode), 3:4 @ d896/ffn4864"
 # Linears that read the same activation run as one fused projection.
 PROJECTIONS = (("qkv", ("q", "k", "v"), "attn_in"), ("o", ("o",), "attn_out"),
@@ -68,7 +71,19 @@ def parse():
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run 4 device copies of MIB MiB (reference for the HBM byte "
                         "counters under rocprofv3) and exit")
+    p.add_argument("--profile-kernels", action="store_true",
+                   help="only launch each hot-path kernel a few times at the benchmark's "
+                        "shapes (for rocprofv3 counter passes) and exit")
     return p.parse_args()
+
+
+def make_flush(torch, dev):
+    """A read of FLUSH_BYTES (twice the Infinity Cache) that evicts the
+    inputs of the kernel timed next, so that working sets under 256 MB are
+    timed from HBM; reads leave clean lines, so the flush adds no
+    write-back to the timed kernel."""
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    return lambda: buf.amax()
 
 
 class Timer:
@@ -207,6 +222,11 @@ def main():
 
     gemm_ops = sum(2.0 * T * N * K for _, N, K in linears)
 
+    if args.profile_kernels:
+        profile_kernels(torch, sbl, synth, dev, refresh, quant_acts, gemm, proj, xq, beta,
+                        packed_f, scale_f)
+        return
+
     # ---------------- timed region ----------------
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -227,29 +247,23 @@ def main():
     log(f"[bench] {ms_per_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f}), {tops:.1f} TOPS")
 
     # ---------------- per-kernel rates (dominant kernel: the product) -------
+    # Each launch is timed from HBM (the Infinity Cache flushed before it):
+    # qkv and o move less than the cache holds.
+    flush = make_flush(torch, dev)
     per_shape = {}
-    tot_ms, tot_ops = 0.0, 0.0
+    tot_ms, tot_ops, tot_bytes = 0.0, 0.0, 0.0
     for name, _, _, N, K in proj:
-        med, mean = timer.time(lambda i=0, nm=name: gemm(nm), 20)
-        ops = 2.0 * T * N * K
-        byts = T * K + N * K / 4 + 4 * N + 4 * T + 4.0 * T * N
-        attain = min(PEAK_I8_TOPS, PEAK_HBM_GBS * 1e9 * ops / byts / 1e12)
-        per_shape[name] = dict(N=N, K=K, T=T, us=mean * 1e3, tops=ops / (mean * 1e-3) / 1e12,
-                               gbs=byts / (mean * 1e-3) / 1e9,
-                               frac_mfma_peak=ops / (mean * 1e-3) / 1e12 / PEAK_I8_TOPS,
-                               frac_attainable=ops / (mean * 1e-3) / 1e12 / attain)
+        med, mean = timer.time(lambda i=0, nm=name: gemm(nm), 20, flush=flush)
+        per_shape[name] = product_rates(T, N, K, n, m, mean)
         tot_ms += mean
-        tot_ops += ops
-    gemm_tops = tot_ops / (tot_ms * 1e-3) / 1e12
+        tot_ops += 2.0 * T * N * K
+        tot_bytes += per_shape[name]["bytes"]
     sha = kernel_sha("gemm.hip", "sbl_device.h")
     tr = load_traffic("prefill_products", sha)
-    roofline = {"kernel": "prefill products (gemm_i8_ws_kernel), mean per launch over the layer's 4: "
-                          "qkv 1152x896, o 896x896, gate_up 9728x896, down 896x4864",
-                "bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_I8_TOPS,
-                "unit": "TFLOP/s", "op": "int8 ops (2*T*N*K, dense-equivalent)",
-                "frac": round(gemm_tops / PEAK_I8_TOPS, 4),
-                "traffic": tr["bytes_per_launch"] if tr else None,
-                "avg_launch_us": round(tot_ms * 1e3 / len(proj), 2)}
+    roofline = product_roofline(tot_ops, tot_bytes, tot_ms, len(proj), n, m,
+                                tr["bytes_per_launch"] if tr else None)
+    roofline["kernel"] = ("prefill products (gemm_i8_ws_kernel), mean per launch over the layer's 4: "
+                          "qkv 1152x896, o 896x896, gate_up 9728x896, down 896x4864 at 32768 tokens")
 
     med_r, mean_r = timer.time(lambda i=0: refresh(), 20)
     nw = sum(N * K for _, N, K in linears)
@@ -263,8 +277,7 @@ def main():
         "useful_tops_n_over_m": round(tops * n / m, 2),
         "step_breakdown_us": {"refresh": round(mean_r * 1e3, 2), "act_quant": round(mean_a * 1e3, 2),
                               "gemm_total": round(tot_ms * 1e3, 2)},
-        "gemm_per_shape": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
-                               for kk, vv in v.items()} for k, v in per_shape.items()},
+        "gemm_per_shape": per_shape,
         "refresh_grouped": {"weights": nw, "us": round(mean_r * 1e3, 2),
                             "gbs": round(refresh_bytes / (mean_r * 1e-3) / 1e9, 1),
                             "frac_hbm": round(refresh_bytes / (mean_r * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
@@ -274,16 +287,8 @@ def main():
     }
 
     if not args.no_extra:
-        extra.update(secondary(torch, sbl, synth, dev, timer))
-        # measured HBM ceilings for context: torch's own fill (write only)
-        # and device copy (read + write) of 1 GiB
-        buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        buf2 = torch.empty_like(buf)
-        _, mf = timer.time(lambda i=0: buf.fill_(1.0), 10)
-        _, mc = timer.time(lambda i=0: buf2.copy_(buf), 10)
-        extra["hbm_ceilings_1GiB"] = {"fill_gbs": round((1 << 30) / (mf * 1e-3) / 1e9, 1),
-                                      "copy_gbs": round((2 << 30) / (mc * 1e-3) / 1e9, 1)}
-        del buf, buf2
+        extra["probes"] = probes(torch, sbl, dev, timer)
+        extra.update(secondary(torch, sbl, synth, dev, timer, flush))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -344,7 +349,75 @@ def graph_time(torch, fns, reps):
     return a.elapsed_time(b) * 1e3 / (reps * len(fns))
 
 
-def secondary(torch, sbl, synth, dev, timer):
+def product_rates(T, N, K, n, m, ms):
+    """Rates of one prefill product launch of `ms` milliseconds against the
+    roof that binds its shape: HBM below the ridge point (algorithmic bytes
+    x~ + codes + scales + beta + fp32 y), the int8 matrix cores above it
+    (the n/m share of the dense products that the method's weights keep)."""
+    ops = 2.0 * T * N * K
+    byts = T * K + N * K / 4 + 4 * N + 4 * T + 4.0 * T * N
+    t = ms * 1e-3
+    bound = "hbm" if ops / byts < RIDGE_OPS_PER_BYTE else "mfma"
+    gbs = byts / t / 1e9
+    useful = ops * n / m / t / 1e12
+    attain_dense = min(PEAK_I8_TOPS, PEAK_HBM_GBS * 1e9 * ops / byts / 1e12)
+    return {"N": N, "K": K, "T": T, "us": round(ms * 1e3, 2), "bytes": int(byts),
+            "ops_per_byte": round(ops / byts, 1), "bound": bound,
+            "gbs": round(gbs, 1), "tops_dense": round(ops / t / 1e12, 1), "tops_useful": round(useful, 1),
+            "frac_binding_roof": round(gbs / PEAK_HBM_GBS if bound == "hbm" else useful / PEAK_I8_TOPS, 4),
+            "frac_attainable_dense": round(ops / t / 1e12 / attain_dense, 4)}
+
+
+def product_roofline(tot_ops, tot_bytes, tot_ms, launches, n, m, traffic):
+    """The dominant kernel's roofline entry, per launch (means over the
+    launches): HBM-bound when the mean launch's ops per byte are below the
+    ridge point (then achieved = algorithmic bytes / time), else bound by
+    the int8 matrix cores (achieved = the kept-weight ops / time)."""
+    t = tot_ms * 1e-3
+    intensity = tot_ops / tot_bytes
+    base = {"avg_launch_us": round(tot_ms * 1e3 / launches, 2),
+            "algorithmic_bytes_per_launch": int(tot_bytes / launches),
+            "dense_ops_per_launch": int(tot_ops / launches),
+            "ops_per_byte": round(intensity, 1), "ridge_ops_per_byte": round(RIDGE_OPS_PER_BYTE, 1),
+            "tops_dense": round(tot_ops / t / 1e12, 1),
+            "tops_useful": round(tot_ops * n / m / t / 1e12, 1),
+            "traffic": traffic}
+    if intensity < RIDGE_OPS_PER_BYTE:
+        gbs = tot_bytes / t / 1e9
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        tops = tot_ops * n / m / t / 1e12
+        r = {"bound": "mfma", "achieved": round(tops, 1), "peak": PEAK_I8_TOPS, "unit": "TOPS",
+             "op": "int8 ops at the kept weights (2*T*N*K*n/m)", "frac": round(tops / PEAK_I8_TOPS, 4)}
+    r.update(base)
+    return r
+
+
+def probes(torch, sbl, dev, timer):
+    """Measured ceilings beside the datasheet peaks: the int8 matrix cores
+    (libsbl's probe kernel, no memory traffic), and HBM through torch's
+    fill (write) and copy (read + write) of 1 GiB."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 8 * cus
+    sink = torch.empty(blocks * 4, dtype=torch.int32, device=dev)
+    iters = 4096
+    ops = sbl.probe_mfma_i8(iters, blocks, sink)
+    _, mp = timer.time(lambda i=0: sbl.probe_mfma_i8(iters, blocks, sink), 10)
+    buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    buf2 = torch.empty_like(buf)
+    _, mf = timer.time(lambda i=0: buf.fill_(1.0), 10)
+    _, mc = timer.time(lambda i=0: buf2.copy_(buf), 10)
+    del buf, buf2
+    res = {"mfma_i8_tops": round(ops / (mp * 1e-3) / 1e12, 1),
+           "mfma_i8_frac_of_datasheet": round(ops / (mp * 1e-3) / 1e12 / PEAK_I8_TOPS, 4),
+           "hbm_fill_1GiB_gbs": round((1 << 30) / (mf * 1e-3) / 1e9, 1),
+           "hbm_copy_1GiB_gbs": round((2 << 30) / (mc * 1e-3) / 1e9, 1)}
+    log(f"[bench] probes: {res}")
+    return res
+
+
+def secondary(torch, sbl, synth, dev, timer, flush):
     res = {}
     # ---- decode sweep: 24 layers x 7 linears, bf16 row scales ----
     log("[bench] decode sweep setup")
@@ -413,6 +486,10 @@ def secondary(torch, sbl, synth, dev, timer):
 
     res["decode_sweep_3of4"] = decode_rates(3)
     res["decode_sweep_2of4"] = decode_rates(2)
+    b1 = res["decode_sweep_3of4"]["B1"]
+    res["decode_roofline"] = {"kernel": "gemv_valu_kernel<1>, the 168-matrix sweep at 1 token, 3:4",
+                              "bound": "hbm", "achieved": b1["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": b1["frac_hbm"], "bytes_per_launch": b1["bytes"], "us": b1["us"]}
     del packed0, scales0
     torch.cuda.empty_cache()
 
@@ -440,12 +517,18 @@ def secondary(torch, sbl, synth, dev, timer):
         xqK, bK = xcache[K]
         img = sbl.sparse24_compress(p)
         yv = torch.empty((T, N), dtype=torch.float32, device=dev)
-        _, md = timer.time(lambda i=0: sbl.sparse_bitlinear_gemm(xqK, bK, p, s, y=yv), 10)
-        _, ms = timer.time(lambda i=0: sbl.sparse_bitlinear_gemm_sparse24(xqK, bK, img, N, s, y=yv), 10)
+        _, md = timer.time(lambda i=0: sbl.sparse_bitlinear_gemm(xqK, bK, p, s, y=yv), 10, flush=flush)
+        _, ms = timer.time(lambda i=0: sbl.sparse_bitlinear_gemm_sparse24(xqK, bK, img, N, s, y=yv), 10,
+                           flush=flush)
         ops = 2.0 * T * N * K
+        # the smfmac roof: 2:4 sparse int8 peak (twice the dense, dense-equivalent ops)
+        byts = T * K + N * K / 4 + 4 * N + 4 * T + 4.0 * T * N
+        t_roof = max(byts / (PEAK_HBM_GBS * 1e9), ops / (2 * PEAK_I8_TOPS * 1e12))
         sp[pname] = {"N": N, "K": K, "dense_us": round(md * 1e3, 2), "smfmac_us": round(ms * 1e3, 2),
+                     "speedup": round(md / ms, 3),
                      "dense_tops": round(ops / (md * 1e-3) / 1e12, 1),
-                     "smfmac_tops": round(ops / (ms * 1e-3) / 1e12, 1)}
+                     "smfmac_tops": round(ops / (ms * 1e-3) / 1e12, 1),
+                     "smfmac_frac_attainable": round(t_roof / (ms * 1e-3), 4)}
         del p, s, img, yv, parts
     res["prefill_2of4_smfmac_vs_dense"] = sp
     log(f"[bench] 2:4: {sp}")
@@ -497,10 +580,9 @@ def secondary(torch, sbl, synth, dev, timer):
         xb = torch.from_numpy(synth.activations_bf16(f"cfg5/x/{K}", Tw, K).view(np.int16)).to(dev)
         xqK, bK = sbl.act_quant_i8(xb)
         yv = torch.empty((Tw, N), dtype=torch.float32, device=dev)
-        _, mg = timer.time(lambda i=0: sbl.sparse_bitlinear_gemm(xqK, bK, j["packed"], j["scale"], y=yv), 10)
-        ops = 2.0 * Tw * N * K
-        g[f"{name}_{N}x{K}"] = {"us": round(mg * 1e3, 2), "tops": round(ops / (mg * 1e-3) / 1e12, 1),
-                                "frac_mfma_peak": round(ops / (mg * 1e-3) / 1e12 / PEAK_I8_TOPS, 4)}
+        _, mg = timer.time(lambda i=0: sbl.sparse_bitlinear_gemm(xqK, bK, j["packed"], j["scale"], y=yv), 10,
+                           flush=flush)
+        g[f"{name}_{N}x{K}"] = product_rates(Tw, N, K, 3, 4, mg)
     wide["gemm"] = g
     res["wide_2048_7168"] = wide
     log(f"[bench] wide: {wide}")
@@ -601,6 +683,71 @@ def secondary(torch, sbl, synth, dev, timer):
 
 
 # --------------------------------------------------------------------------
+def profile_kernels(torch, sbl, synth, dev, refresh, quant_acts, gemm, proj, xq, beta, packed_f,
+                    scale_f):
+    """Each hot-path kernel launched 3 times at the benchmark's shapes, with
+    the Infinity Cache flushed before every launch, for rocprofv3 counter
+    passes (one kernel per dispatch; no timing here)."""
+    flush = make_flush(torch, dev)
+
+    def runs(what, fn, k=3):
+        for _ in range(k):
+            flush()
+            fn()
+        torch.cuda.synchronize()
+        log(f"[profile] {what}")
+
+    runs("grouped refresh of the layer's 7 matrices", refresh)
+    runs("act quant of the layer's 4 inputs", quant_acts)
+    for name, _, _, _, _ in proj:
+        runs(f"product {name}", lambda nm=name: gemm(nm))
+    # 2:4 products on the same fused projections (2:4 codes)
+    T = synth.QWEN05B_PREFILL_TOKENS
+    for name, _, xn, N, K in proj:
+        Wl = torch.from_numpy(synth.latent_weight(f"cfg3/prof/{name}/W", N, K)).to(dev)
+        _, p24, s24, _ = sbl.nm_mask_quant_pack(Wl, 2, 4, want_mask=False, want_bf16=False)
+        del Wl
+        img = sbl.sparse24_compress(p24)
+        yv = torch.empty((T, N), dtype=torch.float32, device=dev)
+        runs(f"2:4 product {name}", lambda: sbl.sparse_bitlinear_gemm_sparse24(xq[xn], beta[xn], img, N, s24, y=yv))
+        del p24, img, yv
+    # decode sweep: 168 matrices, 3:4, bf16 scales
+    mats = [(l, nm, N, K) for l in range(synth.QWEN05B_LAYERS) for nm, N, K in synth.QWEN05B_LINEARS]
+    pk, sc = [], []
+    for (l, nm, N, K) in mats:
+        Wl = torch.from_numpy(synth.latent_weight(f"cfg4/L{l}/{nm}/W", N, K)).to(dev)
+        _, p, _, sb = sbl.nm_mask_quant_pack(Wl, 3, 4, want_mask=False)
+        pk.append(p)
+        sc.append(sb)
+        del Wl
+    for B in synth.DECODE_BATCHES:
+        xK = {}
+        for K in (896, 4864):
+            xb = torch.from_numpy(synth.activations_bf16(f"cfg4/x/{K}/B{B}", B, K).view(np.int16)).to(dev)
+            xK[K] = sbl.act_quant_i8(xb)
+        jobs = [dict(xq=xK[K][0], beta=xK[K][1], packed=pk[i], scale=sc[i],
+                     y=torch.empty((B, N), dtype=torch.float32, device=dev))
+                for i, (_, _, N, K) in enumerate(mats)]
+        h, d = sbl.gemv_descs(jobs)
+        runs(f"decode sweep B={B}", lambda: sbl.sparse_bitlinear_gemv_grouped(h, d, len(mats), B, dev))
+    del pk, sc
+    # operators around the path
+    for K in (896, 4864):
+        xb = torch.from_numpy(synth.activations_bf16(f"cfg2/rms/x/{K}", T, K).view(np.int16)).to(dev)
+        wn = torch.from_numpy(synth.norm_weight(f"cfg2/rms/w/{K}", K)).to(dev)
+        runs(f"rmsnorm act quant K={K}", lambda: sbl.rmsnorm_act_quant_i8(xb, wn, 1e-6))
+    rows_m, cols_m = 16 * 7168, 2048
+    Wm = torch.from_numpy(synth.latent_weight("cfg5/stack/gate/W", rows_m, cols_m)).to(dev)
+    ma = sbl.nm_mask_create(Wm, 3, 4)
+    Wm.add_(1e-4 * torch.randn_like(Wm))
+    mb = sbl.nm_mask_create(Wm, 3, 4)
+    st = torch.empty(2, dtype=torch.int64, device=dev)
+    runs("mask stats", lambda: sbl.nm_mask_stats(ma, mb, rows_m, cols_m, 3, 4, st))
+    _, pw, _, _ = sbl.nm_mask_quant_pack(Wm, 3, 4, want_mask=False)
+    runs("packed codes check", lambda: sbl.packed_codes_check(pw, 3, 4, st))
+    del Wm, ma, mb, pw
+
+
 def cpu_baseline(synth, seconds):
     """The oracle, as it stands, on the host cores: one layer's mask +
     quantise + pack in full, then activation quantisation and the integer

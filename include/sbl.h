@@ -266,9 +266,9 @@ int sparse_bitlinear_gemm_sparse24(const int8_t* xq, const float* beta,
  * Decode product (GEMV), 1 <= T <= 16 tokens; same contract as
  * sparse_bitlinear_gemm, including the optional int32 accumulators.
  * Model card "What does NOT ship" (the serve path needs a kernel that reads
- * the packed layout directly).  Up to 4 tokens run on the vector ALU
- * (int8 dot products), more on the int8 matrix cores; both give the same
- * exact acc and y.
+ * the packed layout directly).  One token with K <= 8192 streams on the
+ * vector ALU (int8 dot products); other cases run on the int8 matrix cores;
+ * both give the same exact acc and y.
  * Errors: SBL_ERR_UNSUPPORTED for T outside [1, 16]; SBL_ERR_SHAPE for
  * N > SBL_GEMV_MAX_ROWS.
  * ------------------------------------------------------------------------ */
@@ -362,6 +362,18 @@ int sparse_bitlinear_ste_backward_noalloc(const float* dy, const int8_t* xq, con
                                           const uint8_t* packed, const float* row_scale,
                                           int64_t T, int64_t K, int64_t N, float* dx, float* dw,
                                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement probe (not part of the operator): the int8 matrix-core rate
+ * the device sustains, for the benchmark's roofline beside the datasheet
+ * peak.  `blocks` blocks of 4 waves; every wave runs 4 independent chains
+ * of `iters` v_mfma_i32_32x32x32_i8 with no memory traffic, i.e.
+ * blocks * 4 * 4 * iters * 65536 int8 operations.  The caller times the
+ * launch on `stream`.
+ *   sink  int32 [blocks * 4] device memory (overwritten)
+ * Errors: SBL_ERR_ARG for iters < 1, blocks < 1 or a NULL sink.
+ * ------------------------------------------------------------------------ */
+int sbl_probe_mfma_i8(int64_t iters, int blocks, int32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

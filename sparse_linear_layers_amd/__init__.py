@@ -98,6 +98,7 @@ def load() -> ctypes.CDLL:
         "sparse_bitlinear_gemm_sparse24": [P, P, P, P, I, I64, I64, I64, P, P, P],
         "sparse_bitlinear_gemv": [P, P, P, P, I, I64, I64, I64, P, P, P],
         "sparse_bitlinear_gemv_grouped": [P, P, I, I64, P],
+        "sbl_probe_mfma_i8": [I64, I, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -356,6 +357,15 @@ def sparse_bitlinear_ste_backward_noalloc(dy, xq, beta, packed, scale,
         _ptr(dy), _ptr(xq), _ptr(beta), _ptr(packed), _ptr(scale), T, K, N, _ptr(dx), _ptr(dw),
         _stream(dy.device)))
     return dx, dw
+
+
+def probe_mfma_i8(iters: int, blocks: int, sink: torch.Tensor) -> int:
+    """Launch the int8 matrix-core probe (measurement only) on the current
+    stream; returns the int8 operations it performs."""
+    _shape(sink, (blocks * 4,), torch.int32, "sink")
+    _check("sbl_probe_mfma_i8", load().sbl_probe_mfma_i8(iters, blocks, _ptr(sink),
+                                                          _stream(sink.device)))
+    return blocks * 4 * 4 * iters * 65536
 
 
 def act_quant_i8(x: torch.Tensor, xq: torch.Tensor | None = None,

@@ -316,4 +316,10 @@ int sparse_bitlinear_ste_backward(const float* dy, const int8_t* xq, const float
                                              need > 0 ? workspace : nullptr, stream));
 }
 
+int sbl_probe_mfma_i8(int64_t iters, int blocks, int32_t* sink, hipStream_t stream) {
+  if (iters < 1 || blocks < 1 || !sink) return SBL_ERR_ARG;
+  (void)hipGetLastError();
+  return hip_status(sbl::launch_probe_mfma_i8(iters, blocks, sink, stream));
+}
+
 }  // extern "C"

@@ -7,12 +7,13 @@
 //
 // The stream of packed codes (1/4 B per weight) is the whole cost.  Two
 // kernels share the contract:
-//  * gemv_valu_kernel<B> (T <= 4): no matrix cores.  Codes are expanded to
-//    int8 with the v_perm table and multiplied with v_dot4 on the vector
-//    ALU; every wave streams its own rows with two k steps of loads in
-//    flight, with no LDS and no barrier (design below).
-//  * gemv_kernel<G> (T > 4): int8 matrix cores (v_mfma_i32_16x16x64_i8)
-//    with the token count in the MFMA's N dimension.
+//  * gemv_stream_kernel (T == 1, K <= 8192): no matrix cores.  Fully
+//    coalesced code loads over whole consecutive rows, v_perm expansion and
+//    v_dot4 products on the vector ALU, row sums through LDS atomics
+//    (design below).
+//  * gemv_kernel<G> (every other case): int8 matrix cores
+//    (v_mfma_i32_16x16x64_i8) with the token count in the MFMA's N
+//    dimension.
 //
 // Design of the matrix-core kernel:
 //  * A unit is 16*G consecutive weight rows of one matrix (G = 4 row groups
@@ -53,6 +54,8 @@ struct GemvArgs {
   int T;
   int block_start[kMaxGroupedGemv + 1];  // first unit of each launch position
   int16_t order[kMaxGroupedGemv];        // launch position -> descriptor index
+  int16_t kblocks[kMaxGroupedGemv];      // launch position -> K / 64
+  int16_t urows[kMaxGroupedGemv];        // launch position -> rows per unit (streaming kernel)
 };
 
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
@@ -69,19 +72,23 @@ struct GemvUnit {
   float* y;
   int32_t* acc;
   int K, N, bf16;
+  int rows;  // rows per unit
   int64_t row0;
 };
 
 typedef const __attribute__((address_space(4))) sbl_gemv_desc* const_desc_ptr;  // scalar loads
 
-// Unit u (ROWS consecutive rows of one matrix) -> its descriptor fields.
-// The launch position of a unit is the last j with block_start[j] <= u:
-// every lane keeps four entries of the table (read once per wave), so a
-// unit's position is four ballots away.
+// Unit u (ROWS consecutive rows of one matrix; ROWS = 0: the launch
+// position's own row count) -> its descriptor fields.  The launch position
+// of a unit is the last j with block_start[j] <= u: every lane keeps four
+// entries of each table (read once per wave), so a unit's position is four
+// ballots away.
 template <int ROWS>
 struct UnitTable {
   int bs[4];   // block_start[q * 64 + lane]
   int ord[4];  // order[q * 64 + lane]
+  int kb[4];   // kblocks[q * 64 + lane]
+  int ur[4];   // urows[q * 64 + lane]
   __device__ __forceinline__ void init(const GemvArgs& a, int lane) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -89,7 +96,20 @@ struct UnitTable {
       const bool in = a.descs && idx < a.count;
       bs[q] = in ? a.block_start[idx] : INT32_MAX;
       ord[q] = in ? a.order[idx] : 0;
+      kb[q] = in ? a.kblocks[idx] : 0;
+      ur[q] = in ? a.urows[idx] : 0;
     }
+  }
+  // launch position of unit u (grouped launches)
+  __device__ __forceinline__ int position(int u) const {
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt += __popcll(__ballot(bs[q] <= u));
+    return cnt - 1;
+  }
+  // K / 64 of unit u's matrix, from the tables alone (no memory access)
+  __device__ __forceinline__ int kblocks_of(const GemvArgs& a, int u) const {
+    return a.descs ? entry(kb, position(u)) : (int)(a.single.K >> 6);
   }
   // entry j (uniform) of a table held four entries per lane
   __device__ __forceinline__ static int entry(const int (&t)[4], int j) {
@@ -100,10 +120,7 @@ struct UnitTable {
   __device__ __forceinline__ GemvUnit fetch(const GemvArgs& a, int u) const {
     GemvUnit f;
     if (a.descs) {
-      int cnt = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) cnt += __popcll(__ballot(bs[q] <= u));
-      const int j = cnt - 1;
+      const int j = position(u);
       const const_desc_ptr dp = (const_desc_ptr)(uintptr_t)a.descs + entry(ord, j);
       f.xq = dp->xq;
       f.beta = dp->beta;
@@ -114,7 +131,8 @@ struct UnitTable {
       f.K = (int)dp->K;
       f.N = (int)dp->N;
       f.bf16 = dp->scale_dtype == SBL_SCALE_BF16;
-      f.row0 = (int64_t)(u - entry(bs, j)) * ROWS;
+      f.rows = ROWS > 0 ? ROWS : entry(ur, j);
+      f.row0 = (int64_t)(u - entry(bs, j)) * f.rows;
     } else {
       f.xq = a.single.xq;
       f.beta = a.single.beta;
@@ -125,7 +143,8 @@ struct UnitTable {
       f.K = (int)a.single.K;
       f.N = (int)a.single.N;
       f.bf16 = a.single.scale_dtype == SBL_SCALE_BF16;
-      f.row0 = (int64_t)u * ROWS;
+      f.rows = ROWS > 0 ? ROWS : a.urows[0];
+      f.row0 = (int64_t)u * f.rows;
     }
     return f;
   }
@@ -135,230 +154,186 @@ static_assert(kMaxGroupedGemv <= 4 * kWave, "four table entries per lane");
 constexpr uint32_t kOut = 0x80000000u;  // a buffer offset past every range: reads 0
 
 // ---------------------------------------------------------------------------
-// Vector-ALU kernel, T <= B tokens (B = 1, 2 or 4).
-//  * A unit is 32 consecutive rows of one matrix and belongs to one wave.
-//    Lanes form 8 groups of 8: group r owns rows r, r+8, r+16, r+24 of the
-//    unit, and lane j of a group reads the 16-byte code chunks j, j+8, ...
-//    of its rows (a k step is one such chunk of every row: 128 contiguous
-//    bytes of 8 rows per load instruction, so every load moves whole cache
-//    lines).  One step of x~ (64 bytes per token) serves the four rows.
-//  * Codes are expanded to int8 in "strided" byte order (11 ALU ops per 16
-//    codes) and x~ is byte-transposed to the same order (8 ops per 16 bytes
-//    per token, shared by the four rows); v_dot4 then adds 4 products per op.
-//  * Waves run independently (no LDS, no barrier) over a flattened sequence
-//    of (unit, k step) with two steps of loads in flight, across unit
-//    boundaries; a wave's units come in snake order over the launch
-//    (longest K first), which evens out the bytes per wave.
-//  * The 8 partial int32 sums of a row (one per lane of its group) are
-//    added with lane exchanges; integer sums are exact in any order.
+// Streaming kernel, one token (T == 1, K <= 8192).
+//  * A unit is `rows` consecutive rows of one matrix (chosen per matrix on
+//    the host so that units carry about equal bytes, about one unit per
+//    resident wave) and belongs to one wave.  Rows are contiguous in
+//    memory, so one load instruction covers whole consecutive rows: with
+//    c = K/64 16-byte chunks per row and c <= 64, lane l reads chunk l % c
+//    of row l / c of a group of 64 / c rows, i.e. bytes 16*l.. of the
+//    group (one contiguous run of whole cache lines); with 64 < c <= 128 a
+//    row takes two instructions (chunks l and 64 + l).  Every lane so keeps
+//    the same one or two chunks of x~ for the whole unit, loaded once and
+//    held in registers in the expanded byte order.
+//  * Four code loads (4 KB) form a step; two steps are in flight.  Codes are
+//    expanded with the v_perm table (11 ops per 16 codes) and multiplied
+//    with v_dot4 (4 products per op).
+//  * A lane's sum for one instruction belongs to one row: the lanes of a
+//    row add theirs into the wave's row accumulators in LDS (integer
+//    atomics: exact in any order; a row of two instructions is summed over
+//    the wave with lane exchanges instead); lane l then finishes rows l and
+//    64 + l.
 // ---------------------------------------------------------------------------
-namespace gv {
-constexpr int ROWS = 32;      // rows per unit
-constexpr int LANES_ROW = 8;  // lanes per row group
-constexpr int RPL = 4;        // rows per lane
-}  // namespace gv
+namespace gs {
+constexpr int MAX_ROWS = 128;    // rows per unit
+constexpr int MAX_CHUNKS = 128;  // K / 64, i.e. K <= 8192
+constexpr int STEP = 4;          // code loads per step
+}  // namespace gs
 
-template <int B>
-__global__ __launch_bounds__(256) void gemv_valu_kernel(GemvArgs a, int units) {
-  using namespace gv;
-  const int lane = threadIdx.x & 63;
-  const int grp = lane >> 3;  // row group
-  const int j = lane & 7;     // chunk lane
-  const int W = (int)gridDim.x * kGemvWaves;
-  const int gw = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kGemvWaves + (int)(threadIdx.x >> 6));
-  const int T = a.T;
+template <bool TWO>  // TWO: a row takes two load instructions (64 < K/64 <= 128)
+__device__ __forceinline__ void stream_unit(const GemvUnit& d, int lane, int* racc) {
+  using namespace gs;
+  const int kbytes = d.K >> 2, cpr = d.K >> 6;
+  const int rpi = TWO ? 1 : 64 / cpr;  // rows per load group
+  const int rows = (int)min((int64_t)d.rows, (int64_t)d.N - d.row0);
+  const int n_instr = ((rows + rpi - 1) / rpi) * (TWO ? 2 : 1);
+  const int nsteps = (n_instr + STEP - 1) / STEP;
+  const int slot = TWO ? 0 : lane / cpr;  // row of the lane within a load group
+  const int kc = TWO ? lane : lane % cpr;
+  const bool act0 = TWO || lane < rpi * cpr;
+  const bool act1 = TWO && 64 + lane < cpr;
 
-  // k-th unit of this wave: round k covers units [kW, kW + W), walked
-  // forwards in even rounds and backwards in odd ones
-  auto unit_at = [&](int k) { return k * W + ((k & 1) ? W - 1 - gw : gw); };
-  if (unit_at(0) >= units) return;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(d.packed + d.row0 * kbytes), (short)0, rows * kbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(d.xq), (short)0, d.K, 0x00020000);
+  const int es = d.bf16 ? 1 : 2;  // log2 of the scale's bytes
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(reinterpret_cast<const char*>(d.row_scale)) + (d.row0 << es), (short)0,
+      rows << es, 0x00020000);
 
-  UnitTable<ROWS> tab;
-  tab.init(a, lane);
+  // x~ chunk(s) of the lane and the scales of the two rows it finishes go
+  // first (the memory counter completes in issue order); both scale types
+  // are requested, the unused one past the end
+  uint4 x0[4], x1[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) x0[p] = bload16(rx, act0 ? (uint32_t)(64 * kc + 16 * p) : kOut);
+  if constexpr (TWO) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) x1[p] = bload16(rx, act1 ? (uint32_t)(64 * (64 + kc) + 16 * p) : kOut);
+  }
+  uint32_t sh[2], sf[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t r = (uint32_t)(lane + 64 * h);
+    sh[h] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(d.bf16 ? r << 1 : kOut), 0, 0);
+    sf[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(d.bf16 ? kOut : r << 2), 0, 0);
+  }
+  const float beta = d.beta[0];
 
-  // One k step's operands.  The row scale of the row the lane stores and
-  // beta ride along with every step (cache hits after the first), so the
-  // epilogue after a unit's last step needs nothing that step did not load
-  // and never waits on the loads in flight behind it.
-  struct Set {
-    uint4 c[RPL];     // code chunk of each of the lane's rows
-    uint4 x[B][4];    // x~ of the chunk: 64 bytes per token
-    uint32_t sh, sf;  // raw row scale: bf16 bits, float bits (the other reads 0)
-    uint32_t bt[B];   // raw beta of each token
-  };
-  // rows past N and chunks past K read as zeros: their offsets are moved
-  // past the end of the resource (an OR of the top bit, no branch)
-  auto load = [&](const GemvUnit& d, int s, Set& S) {
-    const int kbytes = d.K >> 2;
-    const int rows_left = (int)min((int64_t)ROWS, (int64_t)d.N - d.row0);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(d.packed + d.row0 * kbytes), (short)0, rows_left * kbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rx =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(d.xq), (short)0, T * d.K, 0x00020000);
-    const int es = d.bf16 ? 1 : 2;  // log2 of the scale's bytes
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(reinterpret_cast<const char*>(d.row_scale)) + (d.row0 << es), (short)0,
-        rows_left << es, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(d.beta), (short)0, 4 * T, 0x00020000);
-    // Scale and beta first: the memory counter completes in issue order,
-    // so the wait for a step's codes covers them too.  Both scale loads
-    // are issued, the unused one past the end (a load behind a branch would
-    // be waited for inside it).
-    const uint32_t srow = (uint32_t)(grp + 8 * (j >> 1));
-    S.sh = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(d.bf16 ? srow << 1 : kOut), 0, 0);
-    S.sf = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(d.bf16 ? kOut : srow << 2), 0, 0);
+  // code loads of instruction i (rows past the unit's end read zeros)
+  auto load = [&](int s, uint4 (&c)[STEP]) {
 #pragma unroll
-    for (int b = 0; b < B; ++b) S.bt[b] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * b, 0, 0);
-    const int chunk = j + LANES_ROW * s;
-    const uint32_t k_out = chunk < (d.K >> 6) ? 0u : kOut;
-#pragma unroll
-    for (int q = 0; q < RPL; ++q)
-      S.c[q] = bload16(rw, (uint32_t)((grp + 8 * q) * kbytes + 16 * chunk) | k_out);
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        S.x[b][p] = bload16(rx, (uint32_t)(b * d.K + 64 * chunk + 16 * p) | k_out);
+    for (int q = 0; q < STEP; ++q) {
+      const int i = STEP * s + q;
+      const bool seg1 = TWO && (q & 1);  // STEP is even: the segment is q's parity
+      const int grp = TWO ? (i >> 1) : i;
+      const bool on = i < n_instr && (seg1 ? act1 : act0);
+      c[q] = bload16(rw, (uint32_t)(grp * rpi * kbytes + (seg1 ? 1024 : 0) + 16 * lane) | (on ? 0u : kOut));
+    }
   };
 
-  int acc[RPL][B];
-#pragma unroll
-  for (int q = 0; q < RPL; ++q)
-#pragma unroll
-    for (int b = 0; b < B; ++b) acc[q][b] = 0;
+  // accumulators of the unit's rows (and a slot for inactive lanes)
+  racc[lane] = 0;
+  racc[64 + lane] = 0;
+  if (lane == 0) racc[MAX_ROWS] = 0;
 
-  auto compute = [&](const Set& S) {
+  uint4 c0[STEP], c1[STEP];
+  load(0, c0);
+  load(1, c1);
+
+  // x~ in the expanded byte order: transposed 4x4 byte blocks
+  uint32_t xt0[4][4], xt1[4][4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t xt[B][4];
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t in0[4] = {x0[p].x, x0[p].y, x0[p].z, x0[p].w};
+    transpose4x4(in0, xt0[p]);
+    if constexpr (TWO) {
+      const uint32_t in1[4] = {x1[p].x, x1[p].y, x1[p].z, x1[p].w};
+      transpose4x4(in1, xt1[p]);
+    }
+  }
+
+  int prev = 0;  // first half of a row's sum (TWO)
+  auto compute = [&](int s, const uint4 (&c)[STEP]) {
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const uint32_t xin[4] = {S.x[b][p].x, S.x[b][p].y, S.x[b][p].z, S.x[b][p].w};
-        transpose4x4(xin, xt[b]);
-      }
+    for (int q = 0; q < STEP; ++q) {
+      const int i = STEP * s + q;
+      const bool seg1 = TWO && (q & 1);
+      const int grp = TWO ? (i >> 1) : i;
+      int part = 0;
 #pragma unroll
-      for (int q = 0; q < RPL; ++q) {
-        const uint32_t wd = p == 0 ? S.c[q].x : p == 1 ? S.c[q].y : p == 2 ? S.c[q].z : S.c[q].w;
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t wd = p == 0 ? c[q].x : p == 1 ? c[q].y : p == 2 ? c[q].z : c[q].w;
         uint32_t e[4];
         expand16_strided(wd, e);
 #pragma unroll
-        for (int b = 0; b < B; ++b)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) acc[q][b] = __builtin_amdgcn_sdot4((int)e[m], (int)xt[b][m], acc[q][b], false);
+        for (int m = 0; m < 4; ++m)
+          part = __builtin_amdgcn_sdot4((int)e[m], (int)(seg1 ? xt1[p][m] : xt0[p][m]), part, false);
       }
-    }
-  };
-
-  // y (and acc) of the unit.  The 8 lanes of a group hold partial sums of
-  // its 4 rows; three exchange rounds (lane bits 2, 1, 0) halve the rows a
-  // lane keeps and add the partner's share of them, so that lane j ends
-  // with the whole sum of row q = j/2 (both lanes of a pair hold it) and
-  // every lane does the same work.  Lanes with even j store row
-  // grp + 8*(j/2) for every token.
-  auto epilogue = [&](const GemvUnit& d, const Set& S) {
-    const bool hi2 = (j & 4) != 0, hi1 = (j & 2) != 0;
+      if constexpr (TWO) {
+        // one row per instruction pair, all lanes: a wave sum after the
+        // pair's second half (lane exchanges; exact integer adds)
+        if (seg1) {
+          part += prev;
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      // round 1: keep rows {2,3} (bit 2 set) or {0,1}; send the other two
-      const int k0 = hi2 ? acc[2][b] : acc[0][b], k1 = hi2 ? acc[3][b] : acc[1][b];
-      const int s0 = hi2 ? acc[0][b] : acc[2][b], s1 = hi2 ? acc[1][b] : acc[3][b];
-      const int m0 = k0 + __shfl_xor(s0, 4, kWave), m1 = k1 + __shfl_xor(s1, 4, kWave);
-      // round 2: keep one of the two
-      int v = (hi1 ? m1 : m0) + __shfl_xor(hi1 ? m0 : m1, 2, kWave);
-      // round 3: the pair's two halves
-      v += __shfl_xor(v, 1, kWave);
-      acc[0][b] = v;
-    }
-    // Stores go through buffer resources over the unit's rows of each
-    // token row (global-memory stores only, so the counters of the loads in
-    // flight stay exact); rows past N and odd lanes fall outside them.
-    const int rows_left = (int)min((int64_t)ROWS, (int64_t)d.N - d.row0);
-    const uint32_t soff = (j & 1) ? kOut : (uint32_t)(4 * (grp + 8 * (j >> 1)));
-    const float g = __uint_as_float(d.bf16 ? (uint32_t)S.sh << 16 : S.sf);
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      if (b < T) {
-        const int c = acc[0][b];
-        const float bt = __fdiv_rn(__uint_as_float(S.bt[b]), 127.0f);
-        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-            d.y + (int64_t)b * d.N + d.row0, (short)0, 4 * rows_left, 0x00020000);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(((float)c * bt) * g), ry, (int)soff, 0, 0);
-        if (d.acc) {
-          const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-              d.acc + (int64_t)b * d.N + d.row0, (short)0, 4 * rows_left, 0x00020000);
-          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)c, ra, (int)soff, 0, 0);
+          for (int d = 32; d >= 1; d >>= 1) part += __shfl_xor(part, d, kWave);
+          if (lane == 0 && i < n_instr) racc[grp] = part;
+        } else {
+          prev = part;
         }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < RPL; ++q)
-#pragma unroll
-      for (int b = 0; b < B; ++b) acc[q][b] = 0;
-  };
-
-  auto nsteps = [](const GemvUnit& d) { return (d.K + 64 * LANES_ROW - 1) / (64 * LANES_ROW); };
-
-  // load cursor: unit index lk of this wave, step ls of it; it stays on the
-  // last step once the wave's units run out (those loads are never used)
-  int lk = 0, ls = 0;
-  GemvUnit ld = tab.fetch(a, unit_at(0));
-  int lsteps = nsteps(ld);
-  auto advance_load = [&]() {
-    if (++ls == lsteps) {
-      const int u = unit_at(lk + 1);
-      if (u < units) {
-        ++lk;
-        ls = 0;
-        ld = tab.fetch(a, u);
-        lsteps = nsteps(ld);
       } else {
-        ls = lsteps - 1;
+        // the lanes of a row add their sums into its accumulator
+        const bool on = i < n_instr && act0;
+        atomicAdd(&racc[on ? grp * rpi + slot : MAX_ROWS], part);
       }
     }
   };
-  // compute cursor
-  int ck = 0, cs = 0;
-  GemvUnit cd = ld;
-  int csteps = lsteps;
-
-  // steps of all this wave's units: the loop below runs them in pairs with
-  // no exit between the halves (an exit there would make the compiler
-  // assume that either register set may have been loaded last, and wait
-  // for both)
-  int total = 0;
-  for (int k = 0;; ++k) {
-    const int u = unit_at(k);
-    if (u >= units) break;
-    total += nsteps(k == 0 ? ld : tab.fetch(a, u));
+  // Steps in pairs with no exit between the halves (an exit there would
+  // make the compiler assume either register set may have been loaded
+  // last).  The scheduling barriers keep each refill ahead of the next
+  // step's products: the scheduler would otherwise start consuming the
+  // other set first, and wait for every load in flight.
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    compute(s, c0);
+    load(s + 2, c0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s + 1, c1);
+    load(s + 3, c1);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (s < nsteps) compute(s, c0);
 
-  Set s0, s1;
-  load(ld, ls, s0);
-  advance_load();
-  load(ld, ls, s1);
-  advance_load();
-  auto step = [&](Set& S) {
-    compute(S);
-    if (++cs == csteps) {
-      epilogue(cd, S);
-      const int u = unit_at(ck + 1);
-      if (u < units) {
-        ++ck;
-        cs = 0;
-        cd = tab.fetch(a, u);
-        csteps = nsteps(cd);
-      }
-    }
-    load(ld, ls, S);
-    advance_load();
-  };
-  int it = 0;
-  for (; it + 1 < total; it += 2) {
-    step(s0);
-    step(s1);
+  // epilogue: rows lane and 64 + lane; stores through resources over the
+  // unit's rows (rows past its end fall outside them)
+  const float bt = __fdiv_rn(beta, 127.0f);
+  const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(d.y + d.row0, (short)0, 4 * rows, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(d.acc + d.row0, (short)0, 4 * rows, 0x00020000);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = lane + 64 * h;
+    const int c = racc[r];
+    const float g = __uint_as_float(d.bf16 ? sh[h] << 16 : sf[h]);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(((float)c * bt) * g), ry, 4 * r, 0, 0);
+    if (d.acc) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)c, ra, 4 * r, 0, 0);
   }
-  if (it < total) step(s0);
+}
+
+__global__ __launch_bounds__(256) void gemv_stream_kernel(GemvArgs a, int units) {
+  __shared__ int sacc[kGemvWaves][gs::MAX_ROWS + 1];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int W = (int)gridDim.x * kGemvWaves;
+  UnitTable<0> tab;
+  tab.init(a, lane);
+  for (int u = (int)blockIdx.x * kGemvWaves + wv; u < units; u += W) {
+    const GemvUnit d = tab.fetch(a, u);
+    if (d.K > 64 * 64)
+      stream_unit<true>(d, lane, sacc[wv]);
+    else
+      stream_unit<false>(d, lane, sacc[wv]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -530,24 +505,23 @@ static int resident_slots(K kernel, std::atomic<int> (&cache)[kMaxDevices], hipS
   return occ * device_cus(dev);
 }
 
-// Tokens up to which the vector-ALU kernel runs; above, the matrix cores.
-constexpr int64_t kGemvValuMaxTokens = 4;
+// The streaming kernel serves one token and K <= 8192; everything else
+// runs on the matrix cores (units of 64 rows).
+static bool gemv_streams(int64_t T, int64_t maxK) { return T == 1 && maxK <= 64 * gs::MAX_CHUNKS; }
 
-// Rows per unit of the kernel that serves T tokens.
-static int64_t gemv_unit_rows(int64_t T) { return T <= kGemvValuMaxTokens ? gv::ROWS : 64; }
-
-int64_t gemv_blocks(int64_t N, int64_t T) {
-  const int64_t rows = gemv_unit_rows(T);
-  return (N + rows - 1) / rows;
+// Rows per unit of the streaming kernel for a matrix of K columns: about
+// `target` bytes, a whole number of load groups, at most MAX_ROWS.
+static int stream_unit_rows(int64_t K, int64_t target) {
+  const int64_t kbytes = K / 4, cpr = K / 64;
+  const int64_t rpi = cpr > 64 ? 1 : 64 / cpr;
+  const int64_t cap = gs::MAX_ROWS / rpi * rpi;
+  int64_t rows = (target / kbytes + rpi / 2) / rpi * rpi;
+  return (int)std::min(cap, std::max(rpi, rows));
 }
 
-template <int B>
-static hipError_t launch_valu(const GemvArgs& a, int64_t units, hipStream_t stream) {
-  static std::atomic<int> cache[kMaxDevices];
-  const int64_t waves = std::min<int64_t>(units, (int64_t)resident_slots(gemv_valu_kernel<B>, cache, stream) * kGemvWaves);
-  const int grid = (int)((waves + kGemvWaves - 1) / kGemvWaves);
-  hipLaunchKernelGGL(gemv_valu_kernel<B>, dim3((unsigned)grid), dim3(256), 0, stream, a, (int)units);
-  return hipGetLastError();
+int64_t gemv_blocks(int64_t N, int64_t T) {
+  (void)T;
+  return N;  // at least one row per unit: an upper bound on the units of either kernel
 }
 
 hipError_t launch_gemv(const sbl_gemv_desc* host, const sbl_gemv_desc* dev, int count, int64_t T,
@@ -565,24 +539,38 @@ hipError_t launch_gemv(const sbl_gemv_desc* host, const sbl_gemv_desc* dev, int 
     int16_t ord[kMaxGroupedGemv];
     for (int i = 0; i < n; ++i) ord[i] = (int16_t)i;
     std::stable_sort(ord, ord + n, [&](int16_t x, int16_t y) { return host[first + x].K > host[first + y].K; });
+    int64_t maxK = 0, bytes = 0;
+    for (int i = 0; i < n; ++i) {
+      maxK = std::max<int64_t>(maxK, host[first + i].K);
+      bytes += host[first + i].N * (host[first + i].K / 4);
+    }
+    const bool streams = gemv_streams(T, maxK);
+    static std::atomic<int> cache_s[kMaxDevices], cache_m[kMaxDevices];
+    const int64_t slots = streams ? resident_slots(gemv_stream_kernel, cache_s, stream)
+                                  : resident_slots(gemv_kernel<4>, cache_m, stream);
+    const int64_t target = std::max<int64_t>(4096, bytes / std::max<int64_t>(1, slots * kGemvWaves));
     int64_t units = 0;
     for (int i = 0; i < n; ++i) {
+      const sbl_gemv_desc& d = host[first + ord[i]];
+      const int rows = streams ? stream_unit_rows(d.K, target) : 64;
       a.order[i] = ord[i];
+      a.kblocks[i] = (int16_t)(d.K >> 6);
+      a.urows[i] = (int16_t)rows;
       a.block_start[i] = (int)units;
-      units += gemv_blocks(host[first + ord[i]].N, T);
+      units += (d.N + rows - 1) / rows;
     }
     a.block_start[n] = (int)units;
+    if (units > INT32_MAX / 2) return hipErrorInvalidValue;
     if (units > 0) {
-      hipError_t e;
-      if (T <= kGemvValuMaxTokens) {
-        e = T == 1 ? launch_valu<1>(a, units, stream)
-                   : T == 2 ? launch_valu<2>(a, units, stream) : launch_valu<4>(a, units, stream);
+      if (streams) {
+        const int64_t waves = std::min<int64_t>(units, slots * kGemvWaves);
+        hipLaunchKernelGGL(gemv_stream_kernel, dim3((unsigned)((waves + kGemvWaves - 1) / kGemvWaves)),
+                           dim3(256), 0, stream, a, (int)units);
       } else {
-        static std::atomic<int> cache[kMaxDevices];
-        const int grid = (int)std::min<int64_t>(units, (int64_t)resident_slots(gemv_kernel<4>, cache, stream));
-        hipLaunchKernelGGL(gemv_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, a, (int)units);
-        e = hipGetLastError();
+        hipLaunchKernelGGL(gemv_kernel<4>, dim3((unsigned)std::min<int64_t>(units, slots)), dim3(256), 0,
+                           stream, a, (int)units);
       }
+      hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
     first = last;

@@ -109,5 +109,6 @@ hipError_t launch_ste_backward(const float* dy, const int8_t* xq, const float* b
 int64_t gemv_blocks(int64_t N, int64_t T);  // work units of the decode product over N rows
 hipError_t launch_gemv(const sbl_gemv_desc* host, const sbl_gemv_desc* dev_or_null, int count,
                        int64_t T, hipStream_t stream);
+hipError_t launch_probe_mfma_i8(int64_t iters, int blocks, int32_t* sink, hipStream_t stream);
 
 }  // namespace sbl
