@@ -487,7 +487,7 @@ def secondary(torch, sbl, synth, dev, timer, flush):
     res["decode_sweep_3of4"] = decode_rates(3)
     res["decode_sweep_2of4"] = decode_rates(2)
     b1 = res["decode_sweep_3of4"]["B1"]
-    res["decode_roofline"] = {"kernel": "gemv_valu_kernel<1>, the 168-matrix sweep at 1 token, 3:4",
+    res["decode_roofline"] = {"kernel": "gemv_stream_kernel, the 168-matrix sweep at 1 token, 3:4",
                               "bound": "hbm", "achieved": b1["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                               "frac": b1["frac_hbm"], "bytes_per_launch": b1["bytes"], "us": b1["us"]}
     del packed0, scales0

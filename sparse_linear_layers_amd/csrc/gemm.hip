@@ -317,14 +317,30 @@ __global__ __launch_bounds__(256, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_i8_k
 //  * LDS: x~ and expanded codes, 2 stages x 256 rows x 144 B each (147 KB),
 //    plus 4 KB of scales: 151.5 KB of the 160 KB.  Three waves per SIMD leave
 //    168 VGPRs per wave: 128 accumulators and one set of fragments.
-namespace ws {
-constexpr int BO = 256, BT = 256, BK = 128, NT = 768;
-constexpr int MATH = 8;  // math waves (2 per SIMD); the 4 waves after them load
-constexpr int STRIDE = BK + 16;  // bytes per staged row: 16-lane fragment reads hit all 64 banks once
-constexpr int WO = 64, WT = 128;  // math wave tile; the 8 math waves are 4 (o) x 2 (t)
-constexpr int TI = WT / 32, TJ = WO / 32;
-constexpr int XQ = BT / 32;  // 16-byte x~ chunks per loader thread and k step (8)
-}  // namespace ws
+// Layout of the warp-specialised kernel: WsWide, 256 (o) x 256 (t) tiles,
+// 128-code k steps, 8 math + 4 loader waves, one block per CU.  (Two
+// independent blocks per CU on 128 x 256 tiles with 64-code k steps, so
+// that one block's stores overlap the other's products, measured 27%
+// slower on the layer's gate/up projection.)
+template <int BO_, int BK_, int MATH_, int LOADERS_, int BLOCKS_PER_CU_>
+struct WsCfg {
+  static constexpr int BO = BO_, BT = 256, BK = BK_;
+  static constexpr int MATH = MATH_, LOADERS = LOADERS_;
+  static constexpr int NT = 64 * (MATH + LOADERS);
+  static constexpr int LT = 64 * LOADERS;          // loader threads: one weight row each
+  static constexpr int BLOCKS_PER_CU = BLOCKS_PER_CU_;
+  static constexpr int STRIDE = BK + 16;  // bytes per staged row: 16-lane fragment reads hit all 64 banks once
+  static constexpr int WO = 64, WT = 128;  // math wave tile
+  static constexpr int WAVES_O = BO / WO;  // math waves along o
+  static constexpr int TI = WT / 32, TJ = WO / 32;
+  static constexpr int CW = BK / 64;         // 16-byte code chunks per weight row and k step
+  static constexpr int XP = BK / 16;         // 16-byte x~ parts per token row and k step
+  static constexpr int XQ = BT * XP / LT;    // x~ chunks per loader thread and k step
+  static_assert(BO == LT, "one weight row per loader thread");
+  static_assert(WAVES_O * (BT / WT) == MATH, "math waves cover the tile");
+  static_assert(XQ * LT == BT * XP, "x~ chunks split evenly");
+};
+using WsWide = WsCfg<256, 128, 8, 4, 1>;
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0,
 // stores past it are dropped.  Callers keep every offset in the per-lane
@@ -347,9 +363,10 @@ __device__ __forceinline__ void buffer_store4(uint32_t v, __amdgpu_buffer_rsrc_t
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voff, (int)soff, kStoreNonTemporal);
 }
 
-template <bool SCALE_BF16>
-__global__ __launch_bounds__(ws::NT, 1) void gemm_i8_ws_kernel(GemmArgs a) {
-  using namespace ws;
+template <class C, bool SCALE_BF16>
+__global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void gemm_i8_ws_kernel(GemmArgs a) {
+  constexpr int BO = C::BO, BT = C::BT, BK = C::BK, MATH = C::MATH, LT = C::LT, STRIDE = C::STRIDE;
+  constexpr int WO = C::WO, WT = C::WT, TI = C::TI, TJ = C::TJ, CW = C::CW, XP = C::XP, XQ = C::XQ;
   __shared__ __attribute__((aligned(16))) int8_t sX[2][BT * STRIDE];  // x~ rows (tokens)
   __shared__ __attribute__((aligned(16))) int8_t sW[2][BO * STRIDE];  // expanded codes (features)
   __shared__ __attribute__((aligned(16))) float sG[2][BO];            // row scales, by tile parity
@@ -369,7 +386,7 @@ __global__ __launch_bounds__(ws::NT, 1) void gemm_i8_ws_kernel(GemmArgs a) {
 
   if (wave < MATH) {
     // ------------------------------ math waves ------------------------------
-    const int wo = wave & 3, wt = wave >> 2;
+    const int wo = wave % C::WAVES_O, wt = wave / C::WAVES_O;
     v16i acc[TI][TJ];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -455,14 +472,11 @@ __global__ __launch_bounds__(ws::NT, 1) void gemm_i8_ws_kernel(GemmArgs a) {
       _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                    \
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[S][i], wf[S][j], acc[i][j], 0, 0, 0); \
   }
-        SBL_FRAG(0, 0);
-        SBL_MMA(0);
-        SBL_FRAG(0, 1);
-        SBL_MMA(0);
-        SBL_FRAG(0, 2);
-        SBL_MMA(0);
-        SBL_FRAG(0, 3);
-        SBL_MMA(0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 32; ++kk) {
+          SBL_FRAG(0, kk);
+          SBL_MMA(0);
+        }
 #undef SBL_FRAG
 #undef SBL_MMA
         if (++kt == KT) {
@@ -476,19 +490,18 @@ __global__ __launch_bounds__(ws::NT, 1) void gemm_i8_ws_kernel(GemmArgs a) {
     }
   } else {
     // ----------------------------- loader waves -----------------------------
-    // Thread lt stages the 32 bytes (128 codes) of packed row lt at byte
-    // 32*kt, and x~ rows x_row + 32 q (q < 8), bytes x_part..+16 of the
-    // step's 128.  Codes of a k tail (K % 128 == 64) are zeroed when staged,
-    // which makes whatever x~ sits there irrelevant.
+    // Thread lt stages the BK/4 bytes (BK codes) of packed row lt at byte
+    // (BK/4)*kt, and x~ rows x_row + (LT/XP) q (q < XQ), bytes x_part..+16 of
+    // the step's BK.  Codes of a k tail (K % BK != 0) are zeroed when
+    // staged, which makes whatever x~ sits there irrelevant.
     const int lt = tid - MATH * 64;
     const int c_row = lt;
-    const int x_row = lt >> 3, x_part = (lt & 7) * 16;
+    const int x_row = lt / XP, x_part = (lt % XP) * 16;
     const int c_vbase = c_row * kbytes;
     const int x_vbase = x_row * (int)K + x_part;
-    const int x_q = 32 * (int)K;
+    const int x_q = (LT / XP) * (int)K;
     int8_t* const wdst = &sW[0][c_row * STRIDE];
     int8_t* const xdst = &sX[0][x_row * STRIDE + x_part];
-    const int sl = lt;  // scale slot of this thread
 
     int ld_tile = tr.first, ld_kt = 0, ld_par = 0;
     int64_t ld_o0 = 0, ld_t0 = 0;
@@ -504,20 +517,21 @@ __global__ __launch_bounds__(ws::NT, 1) void gemm_i8_ws_kernel(GemmArgs a) {
     // Two register sets; every load is unconditional (past the block's last
     // step the cursor stays on that step), so the compiler can wait for
     // exactly the older set.
-    uint4 c0, c1, d0, d1, x0[XQ], x1[XQ];
-    uint32_t g0, g1, b0, b1;
+    constexpr int NB = (BT + LT - 1) / LT;  // beta entries per loader thread
+    uint4 c0[CW], c1[CW], x0[XQ], x1[XQ];
+    uint32_t g0, g1, b0[NB], b1[NB];
     int kt0, kt1, par0, par1;
 #define SBL_LOAD(S)                                                                     \
   {                                                                                     \
     kt##S = ld_kt;                                                                      \
     par##S = ld_par;                                                                    \
-    c##S = buffer_load16(rc, c_vbase + 32 * ld_kt);                                     \
-    d##S = buffer_load16(rc, c_vbase + 32 * ld_kt + 16);                                \
+    _Pragma("unroll") for (int ci = 0; ci < CW; ++ci) c##S[ci] = buffer_load16(rc, c_vbase + (BK / 4) * ld_kt + 16 * ci); \
     _Pragma("unroll") for (int q = 0; q < XQ; ++q) x##S[q] = buffer_load16(rx, x_vbase + q * x_q + BK * ld_kt); \
-    const int64_t so_ = min(ld_o0 + sl, N - 1);                                         \
+    const int64_t so_ = min(ld_o0 + lt, N - 1);                                         \
     g##S = SCALE_BF16 ? (uint32_t)reinterpret_cast<const uint16_t*>(a.scale)[so_] << 16 \
                       : reinterpret_cast<const uint32_t*>(a.scale)[so_];                \
-    b##S = reinterpret_cast<const uint32_t*>(a.beta)[min(ld_t0 + lt, T - 1)];           \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                   \
+      b##S[nb] = reinterpret_cast<const uint32_t*>(a.beta)[min(ld_t0 + lt + nb * LT, T - 1)]; \
     if (++ld_kt == KT) {                                                                \
       if (ld_tile + tr.step < tr.end) {                                                 \
         ld_kt = 0;                                                                      \
@@ -532,28 +546,20 @@ __global__ __launch_bounds__(ws::NT, 1) void gemm_i8_ws_kernel(GemmArgs a) {
 #define SBL_WRITE(S, buf)                                                               \
   {                                                                                     \
     int8_t* d_ = wdst + (buf) * (BO * STRIDE);                                          \
-    const bool ka_ = 32 * kt##S < kbytes, kb_ = 32 * kt##S + 16 < kbytes;               \
-    uint32_t e_[4];                                                                     \
-    expand16_natural(ka_ ? c##S.x : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(d_) = make_uint4(e_[0], e_[1], e_[2], e_[3]);             \
-    expand16_natural(ka_ ? c##S.y : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(d_ + 16) = make_uint4(e_[0], e_[1], e_[2], e_[3]);        \
-    expand16_natural(ka_ ? c##S.z : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(d_ + 32) = make_uint4(e_[0], e_[1], e_[2], e_[3]);        \
-    expand16_natural(ka_ ? c##S.w : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(d_ + 48) = make_uint4(e_[0], e_[1], e_[2], e_[3]);        \
-    expand16_natural(kb_ ? d##S.x : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(d_ + 64) = make_uint4(e_[0], e_[1], e_[2], e_[3]);        \
-    expand16_natural(kb_ ? d##S.y : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(d_ + 80) = make_uint4(e_[0], e_[1], e_[2], e_[3]);        \
-    expand16_natural(kb_ ? d##S.z : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(d_ + 96) = make_uint4(e_[0], e_[1], e_[2], e_[3]);        \
-    expand16_natural(kb_ ? d##S.w : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(d_ + 112) = make_uint4(e_[0], e_[1], e_[2], e_[3]);       \
+    _Pragma("unroll") for (int ci = 0; ci < CW; ++ci) {                                 \
+      const bool ok_ = (BK / 4) * kt##S + 16 * ci < kbytes;                             \
+      const uint32_t cw_[4] = {c##S[ci].x, c##S[ci].y, c##S[ci].z, c##S[ci].w};         \
+      _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                   \
+        uint32_t e_[4];                                                                 \
+        expand16_natural(ok_ ? cw_[h] : 0u, e_);                                        \
+        *reinterpret_cast<uint4*>(d_ + 64 * ci + 16 * h) = make_uint4(e_[0], e_[1], e_[2], e_[3]); \
+      }                                                                                 \
+    }                                                                                   \
     _Pragma("unroll") for (int q = 0; q < XQ; ++q)                                      \
-      *reinterpret_cast<uint4*>(xdst + (buf) * (BT * STRIDE) + q * 32 * STRIDE) = x##S[q]; \
+      *reinterpret_cast<uint4*>(xdst + (buf) * (BT * STRIDE) + q * (LT / XP) * STRIDE) = x##S[q]; \
     if (kt##S == 0) {                                                                   \
-      sBt[par##S][lt] = __fdiv_rn(__uint_as_float(b##S), 127.0f);                       \
+      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                 \
+        if (lt + nb * LT < BT) sBt[par##S][lt + nb * LT] = __fdiv_rn(__uint_as_float(b##S[nb]), 127.0f); \
       sG[par##S][lt] = __uint_as_float(g##S);                                           \
     }                                                                                   \
   }
@@ -597,24 +603,28 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Layout of the warp-specialised kernel the large products run on.
+using WsMain = WsWide;
+
 hipError_t launch_gemm(const int8_t* xq, const float* beta, const uint8_t* packed,
                        const void* scale, int scale_bf16, int64_t T, int64_t K, int64_t N, float* y,
                        int32_t* acc, hipStream_t stream) {
+  using C = WsMain;
   GemmArgs a{xq, beta, packed, scale, y, acc, T, K, N, scale_bf16, (N % 4) == 0, 0, 0};
-  const int64_t ws_o = (N + ws::BO - 1) / ws::BO, ws_t = (T + ws::BT - 1) / ws::BT;
-  const int cus = device_cus(stream_device(stream));
+  const int64_t ws_o = (N + C::BO - 1) / C::BO, ws_t = (T + C::BT - 1) / C::BT;
+  const int slots = device_cus(stream_device(stream)) * C::BLOCKS_PER_CU;
   if (ws_o * ws_t > INT32_MAX || ((N + 127) / 128) * ((T + 127) / 128) > INT32_MAX)
     return hipErrorInvalidValue;
   // the warp-specialised kernel keeps 32-bit buffer offsets within a tile's
   // rows of y and x~
-  if (ws_o * ws_t >= cus && (int64_t)ws::BT * N * 4 < INT32_MAX / 2) {
+  if (ws_o * ws_t >= slots && (int64_t)C::BT * N * 4 < INT32_MAX / 2) {
     a.tiles_o = (int)ws_o;
     a.ntiles = (int)(ws_o * ws_t);
-    const int grid = (int)std::min<int64_t>(a.ntiles, cus);
+    const int grid = (int)std::min<int64_t>(a.ntiles, slots);
     if (scale_bf16)
-      hipLaunchKernelGGL(gemm_i8_ws_kernel<true>, dim3((unsigned)grid), dim3(ws::NT), 0, stream, a);
+      hipLaunchKernelGGL((gemm_i8_ws_kernel<C, true>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
     else
-      hipLaunchKernelGGL(gemm_i8_ws_kernel<false>, dim3((unsigned)grid), dim3(ws::NT), 0, stream, a);
+      hipLaunchKernelGGL((gemm_i8_ws_kernel<C, false>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
     return hipGetLastError();
   }
   return launch_cfg<128, 128, 2>(a, stream);

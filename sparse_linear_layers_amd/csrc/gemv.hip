@@ -165,7 +165,8 @@ constexpr uint32_t kOut = 0x80000000u;  // a buffer offset past every range: rea
 //    row takes two instructions (chunks l and 64 + l).  Every lane so keeps
 //    the same one or two chunks of x~ for the whole unit, loaded once and
 //    held in registers in the expanded byte order.
-//  * Four code loads (4 KB) form a step; two steps are in flight.  Codes are
+//  * Four code loads (4 KB, non-temporal) form a step; two steps are in
+//    flight.  Codes are
 //    expanded with the v_perm table (11 ops per 16 codes) and multiplied
 //    with v_dot4 (4 products per op).
 //  * A lane's sum for one instruction belongs to one row: the lanes of a
@@ -175,6 +176,9 @@ constexpr uint32_t kOut = 0x80000000u;  // a buffer offset past every range: rea
 //    64 + l.
 // ---------------------------------------------------------------------------
 namespace gs {
+// Codes are read once: the non-temporal policy (bit 1 of the cache-policy
+// operand) streamed the one-token sweep 11% faster.
+constexpr int kLoadNonTemporal = 2;
 constexpr int MAX_ROWS = 128;    // rows per unit
 constexpr int MAX_CHUNKS = 128;  // K / 64, i.e. K <= 8192
 constexpr int STEP = 4;          // code loads per step
@@ -229,7 +233,10 @@ __device__ __forceinline__ void stream_unit(const GemvUnit& d, int lane, int* ra
       const bool seg1 = TWO && (q & 1);  // STEP is even: the segment is q's parity
       const int grp = TWO ? (i >> 1) : i;
       const bool on = i < n_instr && (seg1 ? act1 : act0);
-      c[q] = bload16(rw, (uint32_t)(grp * rpi * kbytes + (seg1 ? 1024 : 0) + 16 * lane) | (on ? 0u : kOut));
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
+          rw, (int)((uint32_t)(grp * rpi * kbytes + (seg1 ? 1024 : 0) + 16 * lane) | (on ? 0u : kOut)), 0,
+          kLoadNonTemporal);
+      c[q] = make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
     }
   };
 
