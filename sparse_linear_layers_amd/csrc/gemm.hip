@@ -291,56 +291,68 @@ __global__ __launch_bounds__(256, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_i8_k
 }
 
 // ---------------------------------------------------------------------------
-// Warp-specialised kernel for problems with at least one tile per CU:
-// 256 (o) x 256 (t) output tiles, 128-code k steps, one persistent 768-thread
-// block per CU.
+// Warp-specialised kernel for problems with at least one tile per block slot:
+// BO (o) x BT (t) output tiles, 128-code k steps, persistent blocks of MATH
+// math waves and LOADERS loader waves (layout in WsCfg).
 //
-//  * Waves 0-7 are math waves (two per SIMD): each holds a 64 (o) x 128 (t)
-//    block of int32 accumulators, reads its MFMA fragments from LDS and
-//    writes its finished outputs itself.  They issue no global loads, so a
-//    math wave never waits on the memory counter for a load queued behind
-//    its own fp32 stores (loads and stores share one in-order counter on
-//    this architecture): the stores of a finished tile drain while the next
-//    tile computes.
-//  * Waves 8-11 are loader waves: they stream x~ and the packed codes of the
-//    k steps two ahead into registers (two register sets), expand the codes
-//    to int8 with the v_perm table while writing them to LDS (double
-//    buffered, one barrier per k step), and stage each tile's row scales and
+//  * Math waves each hold a 64 (o) x 128 (t) block of int32 accumulators,
+//    read their MFMA fragments from LDS and write their finished outputs
+//    themselves.  They issue no global loads, so a math wave never waits on
+//    the memory counter for a load queued behind its own fp32 stores (loads
+//    and stores share one in-order counter on this architecture).
+//  * Loader waves stream x~ and the packed codes of the k steps two ahead
+//    into registers (two register sets) and write them to LDS (double
+//    buffered, one barrier per k step), with each tile's row scales and
 //    beta/127 for the math waves' epilogue.
+//  * The packed codes are staged as they are (a quarter of the bytes of
+//    int8 codes) and expanded by the math waves right before their
+//    products, in the order the three-op expansion produces; the loaders
+//    stage x~ with each 16-byte group transposed 4 x 4 to match.  (Staging
+//    int8 codes expanded by the loaders moved 40% more LDS bytes per step
+//    and measured 4-7% slower.)
 //  * Tokens are the MFMA A operand and weights the B operand, so register r
 //    of a lane holds output (token 8*(r/4) + 4*(lane/32) + r%4, feature
 //    lane%32) of a 32 x 32 block: one dword store per register writes two
-//    whole 128-byte row segments of y, with no transposition.
+//    whole 128-byte row segments of y, with no transposition.  (Weights as
+//    A with one 16-byte store per four features measured 17% slower on the
+//    layer's gate/up projection with the default cache policy, and 3x
+//    slower with the streaming policy: its 32-byte row pieces reach memory
+//    as partial lines.)
 //  * Loads and stores go through buffer resources rebased per tile; rows
 //    past N or T read as zero and their stores are dropped by the hardware
 //    range check.
-//  * LDS: x~ and expanded codes, 2 stages x 256 rows x 144 B each (147 KB),
-//    plus 4 KB of scales: 151.5 KB of the 160 KB.  Three waves per SIMD leave
-//    168 VGPRs per wave: 128 accumulators and one set of fragments.
-// Layout of the warp-specialised kernel: WsWide, 256 (o) x 256 (t) tiles,
-// 128-code k steps, 8 math + 4 loader waves, one block per CU.  (Two
-// independent blocks per CU on 128 x 256 tiles with 64-code k steps, so
-// that one block's stores overlap the other's products, measured 27%
-// slower on the layer's gate/up projection.)
-template <int BO_, int BK_, int MATH_, int LOADERS_, int BLOCKS_PER_CU_>
+template <int BO_, int BT_, int MATH_, int LOADERS_, int BLOCKS_PER_CU_>
 struct WsCfg {
-  static constexpr int BO = BO_, BT = 256, BK = BK_;
+  static constexpr int BO = BO_, BT = BT_, BK = 128;
   static constexpr int MATH = MATH_, LOADERS = LOADERS_;
   static constexpr int NT = 64 * (MATH + LOADERS);
-  static constexpr int LT = 64 * LOADERS;          // loader threads: one weight row each
+  static constexpr int LT = 64 * LOADERS;  // loader threads
   static constexpr int BLOCKS_PER_CU = BLOCKS_PER_CU_;
-  static constexpr int STRIDE = BK + 16;  // bytes per staged row: 16-lane fragment reads hit all 64 banks once
-  static constexpr int WO = 64, WT = 128;  // math wave tile
-  static constexpr int WAVES_O = BO / WO;  // math waves along o
+  // waves each SIMD must hold for BLOCKS_PER_CU blocks per CU (the second
+  // launch bound is a minimum of waves per SIMD, which caps the registers)
+  static constexpr int WAVES_PER_SIMD = (NT / 64 * BLOCKS_PER_CU + 3) / 4;
+  static constexpr int STRIDE = BK + 16;       // bytes per staged x~ row: 16-lane fragment reads hit all 64 banks once
+  static constexpr int WSTRIDE = BK / 4 + 16;  // bytes per staged row of packed codes (same property)
+  static constexpr int WO = 64, WT = 128;      // math wave tile
+  static constexpr int WAVES_O = BO / WO;      // math waves along o
   static constexpr int TI = WT / 32, TJ = WO / 32;
   static constexpr int CW = BK / 64;         // 16-byte code chunks per weight row and k step
+  static constexpr int CR = BO / LT;         // weight rows per loader thread
   static constexpr int XP = BK / 16;         // 16-byte x~ parts per token row and k step
   static constexpr int XQ = BT * XP / LT;    // x~ chunks per loader thread and k step
-  static_assert(BO == LT, "one weight row per loader thread");
+  static constexpr int NB = (BT + LT - 1) / LT;  // beta entries per loader thread
+  static_assert(CR * LT == BO, "weight rows split evenly over the loader threads");
   static_assert(WAVES_O * (BT / WT) == MATH, "math waves cover the tile");
   static_assert(XQ * LT == BT * XP, "x~ chunks split evenly");
 };
-using WsWide = WsCfg<256, 128, 8, 4, 1>;
+// The layout the large products run on: 256 x 256 tiles, 8 math and 4
+// loader waves, one block per CU (three waves per SIMD: 168 VGPRs each).
+// LDS: x~ 2 x 256 x 144 B, codes 2 x 256 x 48 B, scales 4 KB: 100 KB.
+// (Two blocks per CU on 256 x 128 tiles, 4 math + 2 loader waves each, so
+// that one block's stores overlap the other's products, measured 16%
+// slower on the gate/up projection; so did starting half of the blocks
+// half a tile late.)
+using WsMain = WsCfg<256, 256, 8, 4, 1>;
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0,
 // stores past it are dropped.  Callers keep every offset in the per-lane
@@ -355,22 +367,24 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int vof
   return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
 }
 
-// Output stores carry the non-temporal cache policy (bit 1 of the policy
-// operand): y is written once and not read back by the kernel, and streaming
-// it past the caches shortened the fp32-output-bound products by ~10%.
+// Output stores carry the streaming (non-temporal) policy: y is written once
+// and not read back by the kernel, and each store instruction writes whole
+// 128-byte row segments.
 constexpr int kStoreNonTemporal = 2;
 __device__ __forceinline__ void buffer_store4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voff, (int)soff, kStoreNonTemporal);
 }
 
 template <class C, bool SCALE_BF16>
-__global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void gemm_i8_ws_kernel(GemmArgs a) {
-  constexpr int BO = C::BO, BT = C::BT, BK = C::BK, MATH = C::MATH, LT = C::LT, STRIDE = C::STRIDE;
-  constexpr int WO = C::WO, WT = C::WT, TI = C::TI, TJ = C::TJ, CW = C::CW, XP = C::XP, XQ = C::XQ;
-  __shared__ __attribute__((aligned(16))) int8_t sX[2][BT * STRIDE];  // x~ rows (tokens)
-  __shared__ __attribute__((aligned(16))) int8_t sW[2][BO * STRIDE];  // expanded codes (features)
-  __shared__ __attribute__((aligned(16))) float sG[2][BO];            // row scales, by tile parity
-  __shared__ __attribute__((aligned(16))) float sBt[2][BT];           // beta/127, by tile parity
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void gemm_i8_ws_kernel(GemmArgs a) {
+  constexpr int BO = C::BO, BT = C::BT, BK = C::BK, MATH = C::MATH, LT = C::LT;
+  constexpr int STRIDE = C::STRIDE, WSTRIDE = C::WSTRIDE;
+  constexpr int WO = C::WO, WT = C::WT, TI = C::TI, TJ = C::TJ, CW = C::CW, CR = C::CR;
+  constexpr int XP = C::XP, XQ = C::XQ, NB = C::NB;
+  __shared__ __attribute__((aligned(16))) int8_t sX[2][BT * STRIDE];    // x~ rows (tokens)
+  __shared__ __attribute__((aligned(16))) uint8_t sW[2][BO * WSTRIDE];  // packed codes (features)
+  __shared__ __attribute__((aligned(16))) float sG[2][BO];              // row scales, by tile parity
+  __shared__ __attribute__((aligned(16))) float sBt[2][BT];             // beta/127, by tile parity
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -452,33 +466,54 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void gemm_i8_ws_kernel(Gem
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = v16i{};
     };
-
     int tile = tr.first, kt = 0, par = 0;
     __syncthreads();  // step 0 staged
     for (int s = 0; s < total2; ++s) {
       if (s < total) {
         const int buf = s & 1;
-        const int8_t* px = sX[buf] + (wt * WT + (lane & 31)) * STRIDE + (lane >> 5) * 16;
-        const int8_t* pw = sW[buf] + (wo * WO + (lane & 31)) * STRIDE + (lane >> 5) * 16;
-        v4i xf[1][TI], wf[1][TJ];
-#define SBL_FRAG(S, kk)                                                                 \
-  {                                                                                     \
-    _Pragma("unroll") for (int i = 0; i < TI; ++i) xf[S][i] = *reinterpret_cast<const v4i*>(px + i * 32 * STRIDE + (kk) * 32); \
-    _Pragma("unroll") for (int j = 0; j < TJ; ++j) wf[S][j] = *reinterpret_cast<const v4i*>(pw + j * 32 * STRIDE + (kk) * 32); \
-  }
-#define SBL_MMA(S)                                                                      \
-  {                                                                                     \
-    _Pragma("unroll") for (int i = 0; i < TI; ++i)                                      \
-      _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                    \
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[S][i], wf[S][j], acc[i][j], 0, 0, 0); \
-  }
+        // k order inside a step: lane half h takes k in [64h, 64h + 64), and
+        // for product kk its 16 values [64h + 16kk, +16), in the byte order
+        // the code expansion produces (byte j of register m is k = 4j + m of
+        // the 16); x~ is staged in that order, so both operands of every
+        // product see the same k at the same place.  A lane's packed codes
+        // of the whole step are one 16-byte read (dword kk).
+        const int8_t* px = sX[buf] + (wt * WT + (lane & 31)) * STRIDE + (lane >> 5) * 64;
+        const uint8_t* pw = sW[buf] + (wo * WO + (lane & 31)) * WSTRIDE + (lane >> 5) * 16;
+        constexpr int KK = BK / 32;
+        uint4 wc[TJ];
 #pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-          SBL_FRAG(0, kk);
-          SBL_MMA(0);
+        for (int j = 0; j < TJ; ++j) wc[j] = *reinterpret_cast<const uint4*>(pw + j * 32 * WSTRIDE);
+        v4i xf[2];
+        xf[0] = *reinterpret_cast<const v4i*>(px);
+        // The x~ fragment of the next product pair is requested before the
+        // current pair is issued, so every LDS read has two MFMAs (and the
+        // other math waves of the SIMD) to hide behind.
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          v4i wf[TJ];
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            const uint32_t w = kk == 0 ? wc[j].x : kk == 1 ? wc[j].y : kk == 2 ? wc[j].z : wc[j].w;
+            uint32_t e[4];
+            expand16_strided(w, e);
+            wf[j] = v4i{(int)e[0], (int)e[1], (int)e[2], (int)e[3]};
+          }
+#pragma unroll
+          for (int i = 0; i < TI; ++i) {
+            const int c = (kk * TI + i) & 1;
+            if (i + 1 < TI)
+              xf[c ^ 1] = *reinterpret_cast<const v4i*>(px + (i + 1) * 32 * STRIDE + kk * 16);
+            else if (kk + 1 < KK)
+              xf[c ^ 1] = *reinterpret_cast<const v4i*>(px + (kk + 1) * 16);
+            // keep the read above in front of these products (the scheduler
+            // would otherwise sink it to save registers)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xf[c], wf[j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-#undef SBL_FRAG
-#undef SBL_MMA
         if (++kt == KT) {
           epilogue(tile, par);
           kt = 0;
@@ -490,17 +525,18 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void gemm_i8_ws_kernel(Gem
     }
   } else {
     // ----------------------------- loader waves -----------------------------
-    // Thread lt stages the BK/4 bytes (BK codes) of packed row lt at byte
-    // (BK/4)*kt, and x~ rows x_row + (LT/XP) q (q < XQ), bytes x_part..+16 of
-    // the step's BK.  Codes of a k tail (K % BK != 0) are zeroed when
-    // staged, which makes whatever x~ sits there irrelevant.
+    // Thread lt stages the BK/4 bytes (BK codes) at byte (BK/4)*kt of packed
+    // rows lt + LT r (r < CR), and x~ rows x_row + (LT/XP) q (q < XQ), bytes
+    // x_part..+16 of the step's BK, each 16-byte group transposed 4 x 4.
+    // Codes of a k tail (K % BK == 64) are zeroed when staged, which makes
+    // whatever x~ sits there irrelevant.
     const int lt = tid - MATH * 64;
-    const int c_row = lt;
     const int x_row = lt / XP, x_part = (lt % XP) * 16;
-    const int c_vbase = c_row * kbytes;
+    const int c_vbase = lt * kbytes;
+    const int c_r = LT * kbytes;
     const int x_vbase = x_row * (int)K + x_part;
     const int x_q = (LT / XP) * (int)K;
-    int8_t* const wdst = &sW[0][c_row * STRIDE];
+    uint8_t* const wdst = &sW[0][lt * WSTRIDE];
     int8_t* const xdst = &sX[0][x_row * STRIDE + x_part];
 
     int ld_tile = tr.first, ld_kt = 0, ld_par = 0;
@@ -517,19 +553,22 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void gemm_i8_ws_kernel(Gem
     // Two register sets; every load is unconditional (past the block's last
     // step the cursor stays on that step), so the compiler can wait for
     // exactly the older set.
-    constexpr int NB = (BT + LT - 1) / LT;  // beta entries per loader thread
-    uint4 c0[CW], c1[CW], x0[XQ], x1[XQ];
-    uint32_t g0, g1, b0[NB], b1[NB];
+    uint4 c0[CR][CW], c1[CR][CW], x0[XQ], x1[XQ];
+    uint32_t g0[CR], g1[CR], b0[NB], b1[NB];
     int kt0, kt1, par0, par1;
 #define SBL_LOAD(S)                                                                     \
   {                                                                                     \
     kt##S = ld_kt;                                                                      \
     par##S = ld_par;                                                                    \
-    _Pragma("unroll") for (int ci = 0; ci < CW; ++ci) c##S[ci] = buffer_load16(rc, c_vbase + (BK / 4) * ld_kt + 16 * ci); \
+    _Pragma("unroll") for (int r = 0; r < CR; ++r)                                      \
+      _Pragma("unroll") for (int ci = 0; ci < CW; ++ci)                                 \
+        c##S[r][ci] = buffer_load16(rc, c_vbase + r * c_r + (BK / 4) * ld_kt + 16 * ci); \
     _Pragma("unroll") for (int q = 0; q < XQ; ++q) x##S[q] = buffer_load16(rx, x_vbase + q * x_q + BK * ld_kt); \
-    const int64_t so_ = min(ld_o0 + lt, N - 1);                                         \
-    g##S = SCALE_BF16 ? (uint32_t)reinterpret_cast<const uint16_t*>(a.scale)[so_] << 16 \
-                      : reinterpret_cast<const uint32_t*>(a.scale)[so_];                \
+    _Pragma("unroll") for (int r = 0; r < CR; ++r) {                                    \
+      const int64_t so_ = min(ld_o0 + lt + r * LT, N - 1);                              \
+      g##S[r] = SCALE_BF16 ? (uint32_t)reinterpret_cast<const uint16_t*>(a.scale)[so_] << 16 \
+                           : reinterpret_cast<const uint32_t*>(a.scale)[so_];           \
+    }                                                                                   \
     _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                   \
       b##S[nb] = reinterpret_cast<const uint32_t*>(a.beta)[min(ld_t0 + lt + nb * LT, T - 1)]; \
     if (++ld_kt == KT) {                                                                \
@@ -545,22 +584,24 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void gemm_i8_ws_kernel(Gem
   }
 #define SBL_WRITE(S, buf)                                                               \
   {                                                                                     \
-    int8_t* d_ = wdst + (buf) * (BO * STRIDE);                                          \
-    _Pragma("unroll") for (int ci = 0; ci < CW; ++ci) {                                 \
-      const bool ok_ = (BK / 4) * kt##S + 16 * ci < kbytes;                             \
-      const uint32_t cw_[4] = {c##S[ci].x, c##S[ci].y, c##S[ci].z, c##S[ci].w};         \
-      _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                   \
-        uint32_t e_[4];                                                                 \
-        expand16_natural(ok_ ? cw_[h] : 0u, e_);                                        \
-        *reinterpret_cast<uint4*>(d_ + 64 * ci + 16 * h) = make_uint4(e_[0], e_[1], e_[2], e_[3]); \
+    uint8_t* d_ = wdst + (buf) * (BO * WSTRIDE);                                        \
+    _Pragma("unroll") for (int r = 0; r < CR; ++r)                                      \
+      _Pragma("unroll") for (int ci = 0; ci < CW; ++ci) {                               \
+        const bool ok_ = (BK / 4) * kt##S + 16 * ci < kbytes;                           \
+        *reinterpret_cast<uint4*>(d_ + r * LT * WSTRIDE + 16 * ci) =                    \
+            ok_ ? c##S[r][ci] : make_uint4(0u, 0u, 0u, 0u);                             \
       }                                                                                 \
+    _Pragma("unroll") for (int q = 0; q < XQ; ++q) {                                    \
+      const uint32_t in_[4] = {x##S[q].x, x##S[q].y, x##S[q].z, x##S[q].w};             \
+      uint32_t t_[4];                                                                   \
+      transpose4x4(in_, t_);                                                            \
+      *reinterpret_cast<uint4*>(xdst + (buf) * (BT * STRIDE) + q * (LT / XP) * STRIDE) = \
+          make_uint4(t_[0], t_[1], t_[2], t_[3]);                                       \
     }                                                                                   \
-    _Pragma("unroll") for (int q = 0; q < XQ; ++q)                                      \
-      *reinterpret_cast<uint4*>(xdst + (buf) * (BT * STRIDE) + q * (LT / XP) * STRIDE) = x##S[q]; \
     if (kt##S == 0) {                                                                   \
       _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                 \
         if (lt + nb * LT < BT) sBt[par##S][lt + nb * LT] = __fdiv_rn(__uint_as_float(b##S[nb]), 127.0f); \
-      sG[par##S][lt] = __uint_as_float(g##S);                                           \
+      _Pragma("unroll") for (int r = 0; r < CR; ++r) sG[par##S][lt + r * LT] = __uint_as_float(g##S[r]); \
     }                                                                                   \
   }
 
@@ -602,9 +643,6 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, NSET>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
-
-// Layout of the warp-specialised kernel the large products run on.
-using WsMain = WsWide;
 
 hipError_t launch_gemm(const int8_t* xq, const float* beta, const uint8_t* packed,
                        const void* scale, int scale_bf16, int64_t T, int64_t K, int64_t N, float* y,
