@@ -69,6 +69,12 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sbl_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# SBL_SANITIZE=1: built with clang, AddressSanitizer and
+# UndefinedBehaviorSanitizer into liboracle_san.so (same arithmetic flags),
+# for a test run with the clang ASan runtime preloaded.
+_SANITIZE = os.environ.get("SBL_SANITIZE") == "1"
+if _SANITIZE:
+    _LIB_PATH = os.path.join(_HERE, "liboracle_san.so")
 # A test that plants a mistake in a scratch copy of the oracle points here.
 _LIB_OVERRIDE = os.environ.get("SBL_ORACLE_LIB")
 
@@ -86,6 +92,9 @@ def build(verbose: bool = False) -> str:
         "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
         _SRC, "-o", _LIB_PATH + ".tmp", "-lm",
     ]
+    if _SANITIZE:
+        cmd[0:1] = ["/opt/rocm/llvm/bin/clang", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

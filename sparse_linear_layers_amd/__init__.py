@@ -42,7 +42,9 @@ GEMV_MAX_ROWS = 1 << 28
 STE_SCRATCH_BYTES = 64 << 20  # library-owned workspace of the allocation-free backward
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB = os.path.join(_HERE, "libsbl.so")
+# SBL_SANITIZE=1 loads the build whose host code carries ASan/UBSan
+# (sparse_linear_layers_amd.build); device code is the same.
+_LIB = os.path.join(_HERE, "libsbl_san.so" if os.environ.get("SBL_SANITIZE") == "1" else "libsbl.so")
 _lib = None
 
 

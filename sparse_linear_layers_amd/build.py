@@ -9,6 +9,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsbl.so")
+# SBL_SANITIZE=1: the host code (argument checks, launch set-up, caches) is
+# built with AddressSanitizer and UndefinedBehaviorSanitizer into
+# libsbl_san.so, which the binding then loads; device code is unchanged.
+# Run Python with the clang ASan runtime preloaded (see SANITIZE_RUNTIME).
+SANITIZE = os.environ.get("SBL_SANITIZE") == "1"
+LIB_SAN = os.path.join(HERE, "libsbl_san.so")
+SANITIZE_RUNTIME = "/opt/rocm/llvm/lib/clang/22/lib/linux/libclang_rt.asan-x86_64.so"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -26,9 +33,14 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *sources(), "-o", LIB + ".tmp"]
+def build(verbose: bool = False, sanitize: bool = SANITIZE) -> str:
+    out = LIB_SAN if sanitize else LIB
+    san = []
+    if sanitize:
+        san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+               "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    cmd = [HIPCC, *FLAGS, *san, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           *sources(), "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,8 +51,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
     if verbose and msg.strip():
         print(msg)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
