@@ -344,7 +344,8 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(GemvArgs a, int units)
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core kernel (T > 4), units of 16*G rows per block.
+// Matrix-core kernel (every case the streaming kernel does not take), units
+// of 16*G rows per block.
 // ---------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void gemv_kernel(GemvArgs a, int units) {
