@@ -109,7 +109,9 @@ int nm_mask_quant_pack_grouped(const sbl_refresh_desc* descs_host,
     if (!aligned16(d.W) || !aligned16_or_null(d.mask_bits) || !aligned16(d.packed) ||
         !aligned16(d.row_scale) || !aligned16_or_null(d.row_scale_bf16))
       return SBL_ERR_ALIGN;
-    total_blocks += (d.rows + 3) / 4;
+    // rows of 2049..32768 columns take a block each, shorter ones a wave
+    const int64_t need = (d.cols / 4 + 63) / 64;
+    total_blocks += need > 8 && need <= 128 ? d.rows : (d.rows + 3) / 4;
   }
   if (total_blocks > INT32_MAX / 2) return SBL_ERR_ARG;
   (void)hipGetLastError();

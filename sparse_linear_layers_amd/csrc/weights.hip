@@ -79,10 +79,17 @@ __device__ __forceinline__ float4 load_w4_stream(const float4* p, int64_t idx) {
   return make_float4(t.x, t.y, t.z, t.w);
 }
 
-template <int CPL, int MODE>
+// One row per wave (BLOCK = false), or per block of 256 threads for long rows
+// (BLOCK = true: the four waves' double sums meet in LDS in a fixed order).
+// Chunk idx = thread + threads * c, so the chunks of a wave are consecutive
+// and the lane exchanges below (n:8 groups, code and mask packing) stay
+// inside a wave.
+template <int CPL, int MODE, bool BLOCK>
 __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, int n,
                                                bool from_masked) {
+  constexpr int NTH = BLOCK ? 256 : kWave;
   const int lane = lane_id();
+  const int tid = BLOCK ? (int)threadIdx.x : lane;
   const int64_t cols = job.cols;
   const int64_t nchunks = cols >> 2;
   const float4* src = reinterpret_cast<const float4*>(job.W + row * cols);
@@ -90,13 +97,13 @@ __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, i
   uint32_t keep[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    const int64_t idx = lane + (int64_t)kWave * c;
+    const int64_t idx = tid + (int64_t)NTH * c;
     v[c] = idx < nchunks ? load_w4_stream(src, idx) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // ---- mask ----
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    const int64_t idx = lane + (int64_t)kWave * c;
+    const int64_t idx = tid + (int64_t)NTH * c;
     if constexpr (MODE == 0) {
       if (job.mask_in && idx < nchunks) {
         const int64_t bit = row * cols + 4 * idx;
@@ -137,6 +144,12 @@ __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, i
         if (!from_masked || ((keep[c] >> e) & 1u)) s += (double)a[e];
     }
     s = wave_sum(s);
+    if constexpr (BLOCK) {
+      __shared__ double red[4];
+      if (lane == 0) red[threadIdx.x >> 6] = s;
+      __syncthreads();
+      s = (red[0] + red[1]) + (red[2] + red[3]);
+    }
     g = fmaxf((float)(s / (double)cols), 1e-5f);
   }
   // Clip(Round(w/g), -1, 1) is +-1 exactly when |w| > g/2 (g/2 is exact for
@@ -146,7 +159,7 @@ __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, i
   uint32_t* dst = reinterpret_cast<uint32_t*>(job.packed + row * (cols >> 2));
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    const int64_t idx = lane + (int64_t)kWave * c;
+    const int64_t idx = tid + (int64_t)NTH * c;
     const float w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
     uint32_t byte = 0;
 #pragma unroll
@@ -170,7 +183,7 @@ __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, i
       }
     }
   }
-  if (lane == 0) {
+  if (tid == 0) {
     job.scale[row] = g;
     if (job.scale_bf16) job.scale_bf16[row] = f32_to_bf16_rne(g);
   }
@@ -262,7 +275,7 @@ __device__ __forceinline__ void quant_pack_dispatch(const RowJob& job, int64_t r
   if constexpr (CPL == 0)
     quant_pack_row_long<MODE>(job, row, n, from_masked);
   else
-    quant_pack_row<CPL, MODE>(job, row, n, from_masked);
+    quant_pack_row<CPL, MODE, false>(job, row, n, from_masked);
 }
 
 constexpr int kRowsPerBlock = 4;  // one wave per row
@@ -274,13 +287,16 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(RowJob job, int n, int 
   quant_pack_dispatch<CPL, MODE>(job, row, n, from_masked != 0);
 }
 
-// Grouped: the row-blocks of all matrices laid end to end; block_start[d]
-// is the first block of descriptor d (kept in the kernel argument).
+// Grouped: the blocks of all matrices laid end to end; block_start[d] is the
+// first block of entry d (kept in the kernel argument).  An entry's rows
+// take one wave each (four per block), or, for rows longer than 8 chunks
+// per lane (whole_block), one block each.
 struct GroupedRefreshArgs {
   const sbl_refresh_desc* descs;
   int count;
   int block_start[kMaxGroupedRefresh + 1];
-  int descs_idx[kMaxGroupedRefresh];  // index into descs of each entry
+  int descs_idx[kMaxGroupedRefresh];            // index into descs of each entry
+  unsigned char whole_block[kMaxGroupedRefresh];  // one row per block
 };
 
 template <int CPL, int MODE>
@@ -293,9 +309,15 @@ __global__ __launch_bounds__(256) void quant_pack_grouped_kernel(GroupedRefreshA
     if (args.block_start[mid] <= b) lo = mid; else hi = mid - 1;
   }
   const sbl_refresh_desc d = args.descs[args.descs_idx[lo]];
+  RowJob job{d.W, nullptr, d.mask_bits, d.packed, d.row_scale, d.row_scale_bf16, d.rows, d.cols};
+  if constexpr (CPL > 0) {
+    if (args.whole_block[lo]) {  // block-uniform: every wave reaches the barrier inside
+      quant_pack_row<CPL, MODE, true>(job, b - args.block_start[lo], n, from_masked != 0);
+      return;
+    }
+  }
   const int64_t row = (int64_t)(b - args.block_start[lo]) * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= d.rows) return;
-  RowJob job{d.W, nullptr, d.mask_bits, d.packed, d.row_scale, d.row_scale_bf16, d.rows, d.cols};
   quant_pack_dispatch<CPL, MODE>(job, row, n, from_masked != 0);
 }
 
@@ -625,13 +647,38 @@ hipError_t launch_packed_check(const uint8_t* packed, int64_t rows, int64_t cols
 hipError_t launch_quant_pack_grouped(const sbl_refresh_desc* host, const sbl_refresh_desc* dev,
                                      int count, int n, int m, unsigned flags,
                                      hipStream_t stream) {
-  // One launch per register-footprint class (chunks per lane), each over
-  // the descriptors of that class, so a narrow row never carries the
-  // registers of the widest; the block offsets of a launch travel in its
-  // argument block (at most kMaxGroupedRefresh descriptors per launch).
+  // Each matrix gets a register class (16-byte chunks per thread): rows of
+  // up to 8 chunks per lane take one wave per row; longer rows (up to 32
+  // chunks per thread) take a whole block per row; longer still, the
+  // two-pass long-row path.  When no class exceeds 8 chunks (the layers of
+  // both benchmark stacks) every matrix goes into one launch of the largest
+  // class, long-row blocks first; otherwise there is one launch per class,
+  // so a narrow row never carries the registers of the widest.  The block
+  // offsets of a launch travel in its argument block (at most
+  // kMaxGroupedRefresh entries per launch).
   const int fm = (flags & SBL_SCALE_FROM_MASKED) ? 1 : 0;
   constexpr int kClasses[] = {1, 2, 4, 8, 12, 16, 20, 24, 28, 32, 0};
+  auto class_of = [&](int64_t need) {
+    for (int c : kClasses)
+      if (c > 0 && need <= c) return c;
+    return 0;
+  };
+  auto plan = [&](const sbl_refresh_desc& h, bool& whole) {
+    const int64_t need = (h.cols / 4 + kWave - 1) / kWave;
+    whole = need > 8 && need <= 4 * 32;
+    return class_of(whole ? (need + 3) / 4 : need);
+  };
+  int max_cls = 0;
+  bool merge = true;
+  for (int d = 0; d < count; ++d) {
+    if (host[d].rows == 0) continue;
+    bool whole;
+    const int c = plan(host[d], whole);
+    if (c == 0 || c > 8) merge = false;
+    max_cls = std::max(max_cls, c);
+  }
   for (int cls : kClasses) {
+    if (merge && cls != max_cls) continue;
     GroupedRefreshArgs a;
     a.descs = dev;
     int cnt = 0;
@@ -653,16 +700,22 @@ hipError_t launch_quant_pack_grouped(const sbl_refresh_desc* host, const sbl_ref
       blocks = 0;
       return hipSuccess;
     };
-    for (int d = 0; d < count; ++d) {
-      if (chunks_per_lane(host[d].cols) != cls || host[d].rows == 0) continue;
-      if (cnt == kMaxGroupedRefresh) {
-        hipError_t e = flush();
-        if (e != hipSuccess) return e;
+    for (int pass = 0; pass < 2; ++pass) {  // whole-block rows first
+      for (int d = 0; d < count; ++d) {
+        if (host[d].rows == 0) continue;
+        bool whole;
+        const int c = plan(host[d], whole);
+        if ((!merge && c != cls) || whole != (pass == 0)) continue;
+        if (cnt == kMaxGroupedRefresh) {
+          hipError_t e = flush();
+          if (e != hipSuccess) return e;
+        }
+        a.descs_idx[cnt] = d;
+        a.whole_block[cnt] = whole ? 1 : 0;
+        a.block_start[cnt] = (int)blocks;
+        blocks += whole ? host[d].rows : (host[d].rows + kRowsPerBlock - 1) / kRowsPerBlock;
+        ++cnt;
       }
-      a.descs_idx[cnt] = d;
-      a.block_start[cnt] = (int)blocks;
-      blocks += (host[d].rows + kRowsPerBlock - 1) / kRowsPerBlock;
-      ++cnt;
     }
     hipError_t e = flush();
     if (e != hipSuccess) return e;
