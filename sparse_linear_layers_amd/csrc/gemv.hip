@@ -26,8 +26,8 @@
 //    v_mfma_i32_16x16x64_i8, whose lane group l/16 then covers
 //    k = 256*s + 64*(l/16) + 16*i .. +16 on both operands.  The token count
 //    (1..16) rides in the MFMA's N dimension for free.
-//  * Codes are expanded in "strided" byte order (3 ALU ops per 4 weights
-//    instead of 5).  The matching x~ bytes (token l%16, same k) are loaded by
+//  * Codes are expanded in "strided" byte order (9 ALU ops per 16 weights
+//    instead of 19).  The matching x~ bytes (token l%16, same k) are loaded by
 //    each wave straight into registers and byte-transposed once per step;
 //    the same fragments then serve all G row groups, so no LDS staging or
 //    barrier sits in front of the products.
@@ -165,9 +165,10 @@ constexpr uint32_t kOut = 0x80000000u;  // a buffer offset past every range: rea
 //    row takes two instructions (chunks l and 64 + l).  Every lane so keeps
 //    the same one or two chunks of x~ for the whole unit, loaded once and
 //    held in registers in the expanded byte order.
-//  * Four code loads (4 KB, non-temporal) form a step; two steps are in
-//    flight.  Codes are
-//    expanded with the v_perm table (11 ops per 16 codes) and multiplied
+//  * Two code loads (2 KB, non-temporal) form a step; two steps are in
+//    flight (with four loads per step the kernel needed 114 VGPRs and ran
+//    5% slower at four waves per SIMD than this at five).  Codes are
+//    expanded with the v_perm tables (9 ops per 16 codes) and multiplied
 //    with v_dot4 (4 products per op).
 //  * A lane's sum for one instruction belongs to one row: the lanes of a
 //    row add theirs into the wave's row accumulators in LDS (integer
@@ -181,7 +182,7 @@ namespace gs {
 constexpr int kLoadNonTemporal = 2;
 constexpr int MAX_ROWS = 128;    // rows per unit
 constexpr int MAX_CHUNKS = 128;  // K / 64, i.e. K <= 8192
-constexpr int STEP = 4;          // code loads per step
+constexpr int STEP = 2;          // code loads per step
 }  // namespace gs
 
 template <bool TWO>  // TWO: a row takes two load instructions (64 < K/64 <= 128)

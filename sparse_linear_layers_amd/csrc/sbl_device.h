@@ -16,7 +16,8 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // v_perm_b32: result byte i = byte sel_i of the 8-byte value {hi:lo}, where
-// selectors 0-3 address `lo` and 4-7 address `hi`.
+// selectors 0-3 address `lo` and 4-7 address `hi`; selector 8 replicates bit
+// 15 of `lo`, 12 gives 0x00 (and 13 and up 0xFF).
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
@@ -25,14 +26,21 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 // 00 -> 0, 01 -> +1, 10 -> -1 (0xFF), 11 (never written) -> 0.
 constexpr uint32_t kCodeLut = 0x00FF0100u;
 constexpr uint32_t kLow2 = 0x03030303u;
+// The same table for a code held in bits [3:2] of a selector byte, whose
+// values 0, 4, 8, 12 pick: byte 0 of lo (0x00), byte 0 of hi (0x01), bit 15
+// of lo replicated (0xFF), the constant 0x00.
+constexpr uint32_t kCodeLutB2Hi = 0x00000001u;
+constexpr uint32_t kCodeLutB2Lo = 0x00008000u;
 
 // 16 packed codes -> 16 int8 in "strided" order: dword m, byte j holds the
-// code of column 4*j + m.  Three ALU ops per dword.
+// code of column 4*j + m.  Nine ALU ops: codes 1 and 3 of each byte select
+// through the second table without being shifted down.
 __device__ __forceinline__ void expand16_strided(uint32_t w, uint32_t out[4]) {
+  const uint32_t w4 = w >> 4;
   out[0] = perm(kCodeLut, kCodeLut, w & kLow2);
-  out[1] = perm(kCodeLut, kCodeLut, (w >> 2) & kLow2);
-  out[2] = perm(kCodeLut, kCodeLut, (w >> 4) & kLow2);
-  out[3] = perm(kCodeLut, kCodeLut, (w >> 6) & kLow2);
+  out[1] = perm(kCodeLutB2Hi, kCodeLutB2Lo, w & (kLow2 << 2));
+  out[2] = perm(kCodeLut, kCodeLut, w4 & kLow2);
+  out[3] = perm(kCodeLutB2Hi, kCodeLutB2Lo, w4 & (kLow2 << 2));
 }
 
 // Transpose the 4x4 byte matrix held in four dwords: out[j].byte[m] =
