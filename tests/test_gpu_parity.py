@@ -178,6 +178,50 @@ def test_grouped_refresh(sbl):
         _check_quant(W, mask, 0, j["packed"], j["scale"], j["scale_bf16"])
 
 
+
+@pytest.mark.parametrize("n,m,flags", [(3, 4, 0), (6, 8, 0), (3, 4, 1), (4, 8, 1)])
+def test_grouped_refresh_mixed_row_classes(sbl, n, m, flags):
+    """One grouped call over rows of every footprint: short rows (a wave
+    each), rows of 2049..32768 columns (a block each, in one launch with the
+    short ones when no class exceeds 8 chunks, else per class) and rows
+    longer than that (the two-pass path), n:4 and n:8 masks."""
+    shapes = [(33, 9216), (3, 40960), (64, 256), (17, 2112), (100, 896), (7, 4864), (1, 64)]
+    jobs, refs = [], []
+    for i, (r, c) in enumerate(shapes):
+        W = synth.latent_weight(f"gpu/grouped_mixed/{n}{m}/{i}", r, c)
+        jobs.append(dict(W=dev(W), mask=torch.empty(r * c // 8, dtype=torch.uint8, device=DEV),
+                         packed=torch.empty((r, c // 4), dtype=torch.uint8, device=DEV),
+                         scale=torch.empty(r, dtype=torch.float32, device=DEV),
+                         scale_bf16=torch.empty(r, dtype=torch.int16, device=DEV)))
+        refs.append(W)
+    hostd, devd = sbl.refresh_descs(jobs)
+    sbl.nm_mask_quant_pack_grouped(hostd, devd, len(jobs), n, m, flags, DEV)
+    torch.cuda.synchronize()
+    for W, j in zip(refs, jobs):
+        mask = oracle.nm_mask(W, n, m)
+        assert np.array_equal(host(j["mask"]), mask)
+        _check_quant(W, mask, flags, j["packed"], j["scale"], j["scale_bf16"])
+
+
+@pytest.mark.parametrize("n,m", [(3, 4), (2, 8)])
+def test_grouped_refresh_merged_launch(sbl, n, m):
+    """A group whose widest rows need at most 8 chunks per thread (both
+    benchmark stacks' shapes, scaled down): a single launch with whole-block
+    rows first."""
+    shapes = [(40, 2048), (9, 7168), (21, 896), (5, 4864), (2, 2112)]
+    jobs, refs = [], []
+    for i, (r, c) in enumerate(shapes):
+        W = synth.latent_weight(f"gpu/grouped_merged/{n}{m}/{i}", r, c)
+        jobs.append(dict(W=dev(W), packed=torch.empty((r, c // 4), dtype=torch.uint8, device=DEV),
+                         scale=torch.empty(r, dtype=torch.float32, device=DEV)))
+        refs.append(W)
+    hostd, devd = sbl.refresh_descs(jobs)
+    sbl.nm_mask_quant_pack_grouped(hostd, devd, len(jobs), n, m, 0, DEV)
+    torch.cuda.synchronize()
+    for W, j in zip(refs, jobs):
+        _check_quant(W, oracle.nm_mask(W, n, m), 0, j["packed"], j["scale"], None)
+
+
 # -------------------------------------------------------------- act quant
 @pytest.mark.parametrize("T,K", [(1, 64), (3, 256), (128, 896), (77, 4864), (5, 8192), (4, 9216)])
 def test_act_quant(sbl, T, K):
