@@ -304,12 +304,12 @@ __global__ __launch_bounds__(256, 2) void gemm_sp24_kernel(Sp24Args a) {
 //  * Math wave w holds 128 (o) x 64 (t) int32 accumulators (waves 2 (o) x
 //    4 (t) over the tile) and runs two smfmac blocks of 64 k per step.
 //  * Per step and weight row a loader thread reads the 32 image bytes of
-//    the two blocks, expands the four 16-value halves to int8, stored as
-//    [block][row][half] with the halves swapped on rows with bit 3 set (so
-//    the 16-byte fragment reads of 16 consecutive rows hit every bank once),
-//    and stores the four index words as [block][row][half], so one 32-bit
-//    read per lane covers 64 banks.  Every fragment address is then one
-//    per-lane base plus a constant.
+//    the two blocks and stores the four packed 16-value halves and the four
+//    index words as they are, each as [block][row][half] dwords, so one
+//    32-bit read per lane covers 64 banks; the math waves expand a half's
+//    values to int8 right before its smfmac (a quarter of the LDS bytes of
+//    staging int8 values: down 896 x 4864 ran 10% faster).  Every fragment
+//    address is one per-lane base plus a constant.
 //  * Epilogue: the A-operand layout gives lane l token l%32 and four
 //    consecutive features per register group, so each 32 x 32 block passes
 //    through a per-wave LDS patch (row = token) and returns as 16-byte
@@ -319,7 +319,6 @@ namespace spws {
 constexpr int BO = 256, BT = 256, BK = 128, NT = 768;
 constexpr int MATH = 8;
 constexpr int XS = BK + 16;  // bytes per staged x~ row
-constexpr int VS = 32;       // bytes per staged weight row and block: 2 halves of 16 kept values
 constexpr int WO = 128, WT = 64;
 constexpr int TO = WO / 32, TT = WT / 32;
 constexpr int XQ = BT / 32;
@@ -344,7 +343,7 @@ template <bool SCALE_BF16>
 __global__ __launch_bounds__(spws::NT, 1) void gemm_sp24_ws_kernel(Sp24Args a) {
   using namespace spws;
   __shared__ __attribute__((aligned(16))) int8_t sX[2][BT * XS];       // x~ rows (tokens)
-  __shared__ __attribute__((aligned(16))) int8_t sV[2][2][BO * VS];    // expanded kept values
+  __shared__ __attribute__((aligned(16))) uint32_t sV[2][2][BO * 2];   // packed kept values, [row][half]
   __shared__ __attribute__((aligned(16))) uint32_t sI[2][2][BO * 2];   // index words
   __shared__ __attribute__((aligned(16))) float sG[2][BO];             // row scales, by tile parity
   __shared__ __attribute__((aligned(16))) float sBt[2][BT];            // beta/127, by tile parity
@@ -419,7 +418,6 @@ __global__ __launch_bounds__(spws::NT, 1) void gemm_sp24_ws_kernel(Sp24Args a) {
 
     // per-lane fragment bases: weight row wo*WO + l32 (+32 i), half G
     // (swapped on rows with bit 3 set); token row wt*WT + l32 (+32 j)
-    const int a_off = (wo * WO + l32) * VS + 16 * (G ^ ((l32 >> 3) & 1));
     const int i_off = 2 * (wo * WO + l32) + G;
     const int x_off = (wt * WT + l32) * XS + 32 * G;
     auto mma = [&](auto bufc) {
@@ -438,7 +436,11 @@ __global__ __launch_bounds__(spws::NT, 1) void gemm_sp24_ws_kernel(Sp24Args a) {
         }
 #pragma unroll
         for (int i = 0; i < TO; ++i) {
-          const v4i af = *reinterpret_cast<const v4i*>(sV[buf][kb] + a_off + i * 32 * VS);
+          // the row half's 16 kept values, expanded here (a quarter of the
+          // LDS bytes of staging them as int8)
+          uint32_t e[4];
+          expand16_strided(sV[buf][kb][i_off + 64 * i], e);
+          const v4i af = v4i{(int)e[0], (int)e[1], (int)e[2], (int)e[3]};
           const int ix = (int)sI[buf][kb][i_off + 64 * i];
 #pragma unroll
           for (int j = 0; j < TT; ++j)
@@ -480,8 +482,6 @@ __global__ __launch_bounds__(spws::NT, 1) void gemm_sp24_ws_kernel(Sp24Args a) {
     const int c_vbase = lt * rowbytes;
     const int x_vbase = x_row * (int)K + x_part;
     const int x_q = 32 * (int)K;
-    const int sw = (lt >> 3) & 1;
-    int8_t* const vdst = &sV[0][0][lt * VS];
     int8_t* const xdst = &sX[0][x_row * XS + x_part];
 
     int ld_tile = tr.first, ld_kt = 0, ld_par = 0;
@@ -522,17 +522,9 @@ __global__ __launch_bounds__(spws::NT, 1) void gemm_sp24_ws_kernel(Sp24Args a) {
   }
 #define SBL_WRITE(S, buf)                                                               \
   {                                                                                     \
-    int8_t* v_ = vdst + (buf) * (2 * BO * VS);                                          \
     const bool ka_ = 2 * kt##S < KB, kb_ = 2 * kt##S + 1 < KB;                          \
-    uint32_t e_[4];                                                                     \
-    expand16_strided(ka_ ? c##S.x : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(v_ + 16 * sw) = make_uint4(e_[0], e_[1], e_[2], e_[3]);   \
-    expand16_strided(ka_ ? c##S.z : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(v_ + 16 * (1 - sw)) = make_uint4(e_[0], e_[1], e_[2], e_[3]); \
-    expand16_strided(kb_ ? d##S.x : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(v_ + BO * VS + 16 * sw) = make_uint4(e_[0], e_[1], e_[2], e_[3]); \
-    expand16_strided(kb_ ? d##S.z : 0u, e_);                                            \
-    *reinterpret_cast<uint4*>(v_ + BO * VS + 16 * (1 - sw)) = make_uint4(e_[0], e_[1], e_[2], e_[3]); \
+    *reinterpret_cast<uint2*>(&sV[buf][0][2 * lt]) = ka_ ? make_uint2(c##S.x, c##S.z) : make_uint2(0u, 0u); \
+    *reinterpret_cast<uint2*>(&sV[buf][1][2 * lt]) = kb_ ? make_uint2(d##S.x, d##S.z) : make_uint2(0u, 0u); \
     *reinterpret_cast<uint2*>(&sI[buf][0][2 * lt]) = make_uint2(c##S.y, c##S.w);       \
     *reinterpret_cast<uint2*>(&sI[buf][1][2 * lt]) = make_uint2(d##S.y, d##S.w);       \
     _Pragma("unroll") for (int q = 0; q < XQ; ++q)                                      \
