@@ -657,7 +657,10 @@ def secondary(torch, sbl, synth, dev, timer, flush):
         ste[f"{name}_{N}x{K}"] = {
             "dx_us": round(mdx * 1e3, 1), "dw_us": round(mdw * 1e3, 1),
             "dx_tflops": round(fl / (mdx * 1e-3) / 1e12, 1), "dw_tflops": round(fl / (mdw * 1e-3) / 1e12, 1),
-            "frac_bf16_mfma_peak": round(3 * 2 * fl / ((mdx + mdw) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            # the operator's own products against the bf16 peak, and the
+            # matrix-core work (three bf16 pieces per float product)
+            "frac_bf16_peak": round(2 * fl / ((mdx + mdw) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "frac_bf16_mfma_busy_3pieces": round(3 * 2 * fl / ((mdx + mdw) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del dy, xqs, ws
     nxt["ste_backward_T32768"] = ste
     res["next_rows"] = nxt
