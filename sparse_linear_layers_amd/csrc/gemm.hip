@@ -541,12 +541,16 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void gemm_i8_ws_kernel(Ge
 
     int ld_tile = tr.first, ld_kt = 0, ld_par = 0;
     int64_t ld_o0 = 0, ld_t0 = 0;
-    __amdgpu_buffer_rsrc_t rc, rx;
+    __amdgpu_buffer_rsrc_t rc, rx, rg, rb;
+    constexpr int GB = SCALE_BF16 ? 2 : 4;  // bytes per row scale
     auto rebase = [&]() {
       ld_o0 = (int64_t)(ld_tile % a.tiles_o) * BO;
       ld_t0 = (int64_t)(ld_tile / a.tiles_o) * BT;
       rc = buffer_rsrc(a.packed + ld_o0 * kbytes, min((int64_t)BO, N - ld_o0) * kbytes);
       rx = buffer_rsrc(a.xq + ld_t0 * K, min((int64_t)BT, T - ld_t0) * K);
+      // the tile's row scales and beta: entries past N or T read as zero
+      rg = buffer_rsrc(static_cast<const char*>(a.scale) + ld_o0 * GB, min((int64_t)BO, N - ld_o0) * GB);
+      rb = buffer_rsrc(a.beta + ld_t0, min((int64_t)BT, T - ld_t0) * 4);
     };
     rebase();
 
@@ -564,13 +568,12 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void gemm_i8_ws_kernel(Ge
       _Pragma("unroll") for (int ci = 0; ci < CW; ++ci)                                 \
         c##S[r][ci] = buffer_load16(rc, c_vbase + r * c_r + (BK / 4) * ld_kt + 16 * ci); \
     _Pragma("unroll") for (int q = 0; q < XQ; ++q) x##S[q] = buffer_load16(rx, x_vbase + q * x_q + BK * ld_kt); \
-    _Pragma("unroll") for (int r = 0; r < CR; ++r) {                                    \
-      const int64_t so_ = min(ld_o0 + lt + r * LT, N - 1);                              \
-      g##S[r] = SCALE_BF16 ? (uint32_t)reinterpret_cast<const uint16_t*>(a.scale)[so_] << 16 \
-                           : reinterpret_cast<const uint32_t*>(a.scale)[so_];           \
-    }                                                                                   \
+    _Pragma("unroll") for (int r = 0; r < CR; ++r)                                      \
+      g##S[r] = SCALE_BF16                                                              \
+          ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rg, (lt + r * LT) * GB, 0, 0) << 16 \
+          : __builtin_amdgcn_raw_buffer_load_b32(rg, (lt + r * LT) * GB, 0, 0);         \
     _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                   \
-      b##S[nb] = reinterpret_cast<const uint32_t*>(a.beta)[min(ld_t0 + lt + nb * LT, T - 1)]; \
+      b##S[nb] = __builtin_amdgcn_raw_buffer_load_b32(rb, (lt + nb * LT) * 4, 0, 0);    \
     if (++ld_kt == KT) {                                                                \
       if (ld_tile + tr.step < tr.end) {                                                 \
         ld_kt = 0;                                                                      \
@@ -587,9 +590,10 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void gemm_i8_ws_kernel(Ge
     uint8_t* d_ = wdst + (buf) * (BO * WSTRIDE);                                        \
     _Pragma("unroll") for (int r = 0; r < CR; ++r)                                      \
       _Pragma("unroll") for (int ci = 0; ci < CW; ++ci) {                               \
-        const bool ok_ = (BK / 4) * kt##S + 16 * ci < kbytes;                           \
-        *reinterpret_cast<uint4*>(d_ + r * LT * WSTRIDE + 16 * ci) =                    \
-            ok_ ? c##S[r][ci] : make_uint4(0u, 0u, 0u, 0u);                             \
+        /* a chunk past K (K % BK == 64) is overwritten with zeros (uniform) */         \
+        *reinterpret_cast<uint4*>(d_ + r * LT * WSTRIDE + 16 * ci) = c##S[r][ci];       \
+        if ((BK / 4) * kt##S + 16 * ci >= kbytes)                                       \
+          *reinterpret_cast<uint4*>(d_ + r * LT * WSTRIDE + 16 * ci) = make_uint4(0u, 0u, 0u, 0u); \
       }                                                                                 \
     _Pragma("unroll") for (int q = 0; q < XQ; ++q) {                                    \
       const uint32_t in_[4] = {x##S[q].x, x##S[q].y, x##S[q].z, x##S[q].w};             \
