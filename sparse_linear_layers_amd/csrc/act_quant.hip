@@ -21,6 +21,30 @@ __device__ __forceinline__ uint4 load_x16(const uint4* p, int64_t idx) {
   return make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
 }
 
+// x~ codes of 8 values: Clip(Round(v * s), -128, 127) as bytes.  The product
+// is rounded to float, then 1.5 * 2^23 is added: the sum's unit in the last
+// place is 1, so the addition rounds v * s to the nearest integer, ties to
+// even, as rintf does, and the low byte of the sum's bits is that integer in
+// two's complement.  With s = 127 / beta and beta >= max |v|, |v * s| stays
+// below 127.5, so the clip never acts and the byte is the code.
+__device__ __forceinline__ uint2 quant8_codes(const float (&v)[8], float s) {
+  constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+  uint32_t q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = v[e] * s;  // rounded to float first (no contraction)
+    q[e] = __float_as_uint(p + kRound);
+  }
+  uint32_t out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = perm(q[4 * h + 1], q[4 * h], 0x0C0C0400u);      // bytes q0, q1
+    const uint32_t hi = perm(q[4 * h + 3], q[4 * h + 2], 0x0C0C0400u);  // bytes q2, q3
+    out[h] = perm(hi, lo, 0x05040100u);
+  }
+  return make_uint2(out[0], out[1]);
+}
+
 template <int CPL>  // 8-element (16-byte) chunks per lane; 0 = long-row loop
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x,
                                                         int64_t tokens, int64_t cols,
@@ -32,38 +56,36 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   const int64_t nchunks = cols >> 3;
   const uint4* src = reinterpret_cast<const uint4*>(x + t * cols);
   uint2* dst = reinterpret_cast<uint2*>(xq + t * cols);
-  auto chunk_max = [](const uint4& d, uint32_t m) {
+  // max of the magnitude bits of both bf16 halves of each dword, kept per
+  // half in packed 16-bit lanes (folded to one value after the loop)
+  auto chunk_max = [](const uint4& d, us2 m) {
     const uint32_t w[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+    for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[i] & 0x7fff7fffu));
     return m;
   };
+  auto fold = [](us2 m) { return (uint32_t)max(m.x, m.y); };
   auto quant8 = [](const uint4& d, float s) {
     const uint32_t w[4] = {d.x, d.y, d.z, d.w};
-    uint32_t out[2] = {0u, 0u};
+    float f[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float f = __uint_as_float(h ? (w[i] & 0xffff0000u) : (w[i] << 16));
-        float q = rintf(f * s);
-        q = fminf(fmaxf(q, -128.f), 127.f);
-        const uint32_t b = (uint32_t)(int32_t)q & 0xffu;
-        out[i >> 1] |= b << (8 * (2 * (i & 1) + h));
-      }
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
-    return make_uint2(out[0], out[1]);
+    return quant8_codes(f, s);
   };
-  uint32_t m = 0;
+  us2 mh = {0, 0};
+  uint32_t m;
   if constexpr (CPL > 0) {
     uint4 v[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int64_t idx = lane + (int64_t)kWave * c;
       v[c] = idx < nchunks ? load_x16(src, idx) : make_uint4(0u, 0u, 0u, 0u);
-      m = chunk_max(v[c], m);
+      mh = chunk_max(v[c], mh);
     }
-    m = wave_max(m);
+    m = wave_max_dpp(fold(mh));
     const float b = fmaxf(__uint_as_float(m << 16), 1e-5f);
     const float s = __fdiv_rn(127.0f, b);
 #pragma unroll
@@ -75,9 +97,9 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   } else {
     for (int64_t base = 0; base < nchunks; base += kWave) {
       const int64_t idx = base + lane;
-      if (idx < nchunks) m = chunk_max(src[idx], m);
+      if (idx < nchunks) mh = chunk_max(src[idx], mh);
     }
-    m = wave_max(m);
+    m = wave_max_dpp(fold(mh));
     const float b = fmaxf(__uint_as_float(m << 16), 1e-5f);
     const float s = __fdiv_rn(127.0f, b);
     for (int64_t base = 0; base < nchunks; base += kWave) {
@@ -94,11 +116,13 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
 // absmax step ("Mathematical Formulation", step 4; "End-to-End
 // Implementation").  One pass over x: the row stays in registers while
 //   r  = float(1 / sqrt(sum x^2 / cols + eps))   (exact squares, double lane
-//        partials + butterfly, the rest in double, one rounding to float;
-//        0 when the root's argument is 0),
+//        partials (two chains each) summed across the wave by DPP exchanges,
+//        the rest in double, one rounding to float; 0 when the root's
+//        argument is 0),
 //   n  = (x * r) * w             (two float multiplies),
 // then beta, s and x~ exactly as act_quant_kernel does on n.  The weight
-// (4 B per channel) is shared by every token and stays in L2.
+// (4 B per channel) is shared by every token and stays in L2; a lane
+// requests its weights together with its x chunks.
 // ---------------------------------------------------------------------------
 template <int CPL>  // 8-element chunks per lane; 0 = long rows (three passes)
 __global__ __launch_bounds__(256) void rmsnorm_act_quant_kernel(const uint16_t* __restrict__ x,
@@ -122,12 +146,13 @@ __global__ __launch_bounds__(256) void rmsnorm_act_quant_kernel(const uint16_t* 
       f[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
     }
   };
-  auto chunk_ss = [&](const uint4& d, double s) {
+  // exact squares in double (a float square can overflow or lose bits),
+  // even and odd elements summed in two chains
+  auto chunk_ss = [&](const uint4& d, double (&s)[2]) {
     float f[8];
     widen(d, f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += (double)f[e] * (double)f[e];
-    return s;
+    for (int e = 0; e < 8; ++e) s[e & 1] += (double)f[e] * (double)f[e];
   };
   auto normalise = [&](const uint4& d, int64_t idx, float r, float (&n)[8]) {
     float f[8];
@@ -137,21 +162,20 @@ __global__ __launch_bounds__(256) void rmsnorm_act_quant_kernel(const uint16_t* 
 #pragma unroll
     for (int e = 0; e < 8; ++e) n[e] = (f[e] * r) * wv[e];
   };
-  auto nmax = [](const float (&n)[8], uint32_t m) {
+  auto normalise_w = [&](const uint4& d, const float4 (&wq)[2], float r, float (&n)[8]) {
+    float f[8];
+    widen(d, f);
+    const float wv[8] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w, wq[1].x, wq[1].y, wq[1].z, wq[1].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = max(m, __float_as_uint(n[e]) & 0x7fffffffu);
+    for (int e = 0; e < 8; ++e) n[e] = (f[e] * r) * wv[e];
+  };
+  // max |n| as a float (finite, non-negative: ordered like its bits)
+  auto nmax = [](const float (&n)[8], float m) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(n[e]));
     return m;
   };
-  auto quant8 = [](const float (&n)[8], float s) {
-    uint32_t out[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float q = rintf(n[e] * s);
-      q = fminf(fmaxf(q, -128.f), 127.f);
-      out[e >> 2] |= ((uint32_t)(int32_t)q & 0xffu) << (8 * (e & 3));
-    }
-    return make_uint2(out[0], out[1]);
-  };
+  auto quant8 = [](const float (&n)[8], float s) { return quant8_codes(n, s); };
   // r = float(1 / sqrt(sum/cols + eps)) in double (correctly rounded divide
   // and root), one rounding to float; 0 for an all-zero row at eps = 0
   auto inv_rms = [&](double ss) {
@@ -159,26 +183,38 @@ __global__ __launch_bounds__(256) void rmsnorm_act_quant_kernel(const uint16_t* 
     return d > 0.0 ? (float)(1.0 / sqrt(d)) : 0.0f;
   };
   if constexpr (CPL > 0) {
+    // With at most two chunks per lane, the lane's weights are requested
+    // together with its x chunks (a longer row would hold too many
+    // registers: 183 instead of 122 VGPRs at ten chunks).
+    constexpr bool kEarlyW = CPL <= 2;
     uint4 v[CPL];
-    double ss = 0.0;
+    float4 wl[kEarlyW ? CPL : 1][2];
+    double ss[2] = {0.0, 0.0};
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int64_t idx = lane + (int64_t)kWave * c;
-      v[c] = idx < nchunks ? load_x16(src, idx) : make_uint4(0u, 0u, 0u, 0u);
-      ss = chunk_ss(v[c], ss);
+      const bool in = idx < nchunks;
+      v[c] = in ? load_x16(src, idx) : make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (kEarlyW) {
+        wl[c][0] = in ? wsrc[2 * idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+        wl[c][1] = in ? wsrc[2 * idx + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
-    const float r = inv_rms(wave_sum(ss));
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) chunk_ss(v[c], ss);
+    const float r = inv_rms(wave_sum_dpp(ss[0] + ss[1]));
     float n[CPL][8];
-    uint32_t m = 0;
+    float mf = 0.f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int64_t idx = lane + (int64_t)kWave * c;
       if (idx < nchunks) {
-        normalise(v[c], idx, r, n[c]);
-        m = nmax(n[c], m);
+        if constexpr (kEarlyW) normalise_w(v[c], wl[c], r, n[c]);
+        else normalise(v[c], idx, r, n[c]);
+        mf = nmax(n[c], mf);
       }
     }
-    m = wave_max(m);
+    const uint32_t m = wave_max_dpp(__float_as_uint(mf));
     const float b = fmaxf(__uint_as_float(m), 1e-5f);
     const float s = __fdiv_rn(127.0f, b);
 #pragma unroll
@@ -188,22 +224,22 @@ __global__ __launch_bounds__(256) void rmsnorm_act_quant_kernel(const uint16_t* 
     }
     if (lane == 0) beta[t] = b;
   } else {
-    double ss = 0.0;
+    double ss[2] = {0.0, 0.0};
     for (int64_t base = 0; base < nchunks; base += kWave) {
       const int64_t idx = base + lane;
-      if (idx < nchunks) ss = chunk_ss(src[idx], ss);
+      if (idx < nchunks) chunk_ss(src[idx], ss);
     }
-    const float r = inv_rms(wave_sum(ss));
-    uint32_t m = 0;
+    const float r = inv_rms(wave_sum_dpp(ss[0] + ss[1]));
+    float mf = 0.f;
     for (int64_t base = 0; base < nchunks; base += kWave) {
       const int64_t idx = base + lane;
       if (idx < nchunks) {
         float n[8];
         normalise(src[idx], idx, r, n);
-        m = nmax(n, m);
+        mf = nmax(n, mf);
       }
     }
-    m = wave_max(m);
+    const uint32_t m = wave_max_dpp(__float_as_uint(mf));
     const float b = fmaxf(__uint_as_float(m), 1e-5f);
     const float s = __fdiv_rn(127.0f, b);
     for (int64_t base = 0; base < nchunks; base += kWave) {

@@ -118,7 +118,7 @@ __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, i
       uint32_t mine[4] = {abs_key(v[c].x), abs_key(v[c].y), abs_key(v[c].z), abs_key(v[c].w)};
       uint32_t other[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) other[e] = (uint32_t)shfl_xor((int)mine[e], 1);
+      for (int e = 0; e < 4; ++e) other[e] = dpp_u32<kDppXor1>(mine[e]);
       const bool low_half = (lane & 1) == 0;
       uint32_t key[8];
 #pragma unroll
@@ -130,7 +130,7 @@ __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, i
       keep[c] = low_half ? (k8 & 0xFu) : (k8 >> 4);
     }
   }
-  // ---- scale: sum of |w| in double, lane partials then a butterfly ----
+  // ---- scale: sum of |w| in double, lane partials then DPP exchanges ----
   float g;
   if (job.scale_in) {
     g = job.scale_in[row];
@@ -143,7 +143,7 @@ __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, i
       for (int e = 0; e < 4; ++e)
         if (!from_masked || ((keep[c] >> e) & 1u)) s += (double)a[e];
     }
-    s = wave_sum(s);
+    s = wave_sum_dpp(s);
     if constexpr (BLOCK) {
       __shared__ double red[4];
       if (lane == 0) red[threadIdx.x >> 6] = s;
@@ -169,15 +169,15 @@ __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, i
       byte |= f << (2 * e);
     }
     uint32_t word = byte << (8 * (lane & 3));
-    word |= (uint32_t)shfl_xor((int)word, 1);
-    word |= (uint32_t)shfl_xor((int)word, 2);
+    word |= dpp_u32<kDppXor1>(word);
+    word |= dpp_u32<kDppXor2>(word);
     if ((lane & 3) == 0 && idx < nchunks) dst[idx >> 2] = word;
     if constexpr (MODE != 0) {
       if (job.mask_out) {
         uint32_t mw = keep[c] << (4 * (lane & 7));
-        mw |= (uint32_t)shfl_xor((int)mw, 1);
-        mw |= (uint32_t)shfl_xor((int)mw, 2);
-        mw |= (uint32_t)shfl_xor((int)mw, 4);
+        mw |= dpp_u32<kDppXor1>(mw);
+        mw |= dpp_u32<kDppXor2>(mw);
+        mw |= dpp_u32<kDppHalfMirror>(mw);  // the other quad of the 8 lanes
         if ((lane & 7) == 0 && idx < nchunks)
           reinterpret_cast<uint32_t*>(job.mask_out)[(row * cols + 4 * idx) >> 5] = mw;
       }
@@ -208,7 +208,7 @@ __device__ void quant_pack_row_long(const RowJob& job, int64_t row, int n, bool 
     } else {
       uint32_t mine[4] = {abs_key(x.x), abs_key(x.y), abs_key(x.z), abs_key(x.w)};
       uint32_t other[4];
-      for (int e = 0; e < 4; ++e) other[e] = (uint32_t)shfl_xor((int)mine[e], 1);
+      for (int e = 0; e < 4; ++e) other[e] = dpp_u32<kDppXor1>(mine[e]);
       const bool low_half = (lane & 1) == 0;
       uint32_t key[8];
       for (int e = 0; e < 4; ++e) {
@@ -232,7 +232,7 @@ __device__ void quant_pack_row_long(const RowJob& job, int64_t row, int n, bool 
       for (int e = 0; e < 4; ++e)
         if (!from_masked || ((k >> e) & 1u)) s += (double)a[e];
     }
-    s = wave_sum(s);
+    s = wave_sum_dpp(s);
     g = fmaxf((float)(s / (double)cols), 1e-5f);
   }
   const float thr = g * 0.5f;
@@ -249,15 +249,15 @@ __device__ void quant_pack_row_long(const RowJob& job, int64_t row, int n, bool 
       byte |= f << (2 * e);
     }
     uint32_t word = byte << (8 * (lane & 3));
-    word |= (uint32_t)shfl_xor((int)word, 1);
-    word |= (uint32_t)shfl_xor((int)word, 2);
+    word |= dpp_u32<kDppXor1>(word);
+    word |= dpp_u32<kDppXor2>(word);
     if ((lane & 3) == 0 && idx < nchunks) dst[idx >> 2] = word;
     if constexpr (MODE != 0) {
       if (job.mask_out) {
         uint32_t mw = k << (4 * (lane & 7));
-        mw |= (uint32_t)shfl_xor((int)mw, 1);
-        mw |= (uint32_t)shfl_xor((int)mw, 2);
-        mw |= (uint32_t)shfl_xor((int)mw, 4);
+        mw |= dpp_u32<kDppXor1>(mw);
+        mw |= dpp_u32<kDppXor2>(mw);
+        mw |= dpp_u32<kDppHalfMirror>(mw);  // the other quad of the 8 lanes
         if ((lane & 7) == 0 && idx < nchunks)
           reinterpret_cast<uint32_t*>(job.mask_out)[(row * cols + 4 * idx) >> 5] = mw;
       }
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(256) void row_abs_sum_kernel(RowJob job, int n, int
       } else {
         uint32_t mine[4] = {abs_key(x.x), abs_key(x.y), abs_key(x.z), abs_key(x.w)};
         uint32_t other[4];
-        for (int e = 0; e < 4; ++e) other[e] = (uint32_t)shfl_xor((int)mine[e], 1);
+        for (int e = 0; e < 4; ++e) other[e] = dpp_u32<kDppXor1>(mine[e]);
         const bool low_half = (lane & 1) == 0;
         uint32_t key[8];
         for (int e = 0; e < 4; ++e) {
