@@ -8,6 +8,7 @@
 // 1 B/element out).  The absmax is an integer max over the magnitude bits,
 // exact and order-free.
 #include "sbl_device.h"
+#include "sbl_wave.h"
 #include "sbl_launch.h"
 
 namespace sbl {

@@ -12,6 +12,7 @@
 // so W is read exactly once even though the scale must be known before any
 // code is decided.
 #include "sbl_device.h"
+#include "sbl_wave.h"
 #include "sbl_launch.h"
 
 namespace sbl {
