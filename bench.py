@@ -690,10 +690,13 @@ def profile_kernels(torch, sbl, synth, dev, refresh, quant_acts, gemm, proj, xq,
                     scale_f):
     """Each hot-path kernel launched 3 times at the benchmark's shapes, with
     the Infinity Cache flushed before every launch, for rocprofv3 counter
-    passes (one kernel per dispatch; no timing here)."""
+    passes (one kernel per dispatch; no timing here).  Each group starts
+    with one more launch that the summaries leave out: the first launch of a
+    kernel in a process also pays for loading its code."""
     flush = make_flush(torch, dev)
 
     def runs(what, fn, k=3):
+        fn()
         for _ in range(k):
             flush()
             fn()
