@@ -381,7 +381,12 @@ __global__ __launch_bounds__(spws::NT, 1) void gemm_sp24_ws_kernel(Sp24Args a) {
       const __amdgpu_buffer_rsrc_t ra =
           sp_rsrc(a.acc ? static_cast<const void*>(a.acc + t0 * N) : a.y, a.acc ? rows_t * N * 4 : 0);
       int8_t* const e = sE[wave];
-      const int rr = lane >> 3, cc = lane & 7;  // read-back: rows rr + 8v, 16-byte unit cc
+      // the patch addresses are recomputed here from an opaque copy of the
+      // lane (kept live through the products they would spill)
+      int ln = lane;
+      __asm__ volatile("" : "+v"(ln));
+      const int G = ln >> 5, l32 = ln & 31;
+      const int rr = ln >> 3, cc = ln & 7;  // read-back: rows rr + 8v, 16-byte unit cc
 #pragma unroll
       for (int i = 0; i < TO; ++i) {
         const int ol = wo * WO + i * 32 + 4 * cc;
