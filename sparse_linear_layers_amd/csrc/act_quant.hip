@@ -22,6 +22,28 @@ __device__ __forceinline__ uint4 load_x16(const uint4* p, int64_t idx) {
   return make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
 }
 
+// The short-row kernels address a token's row through buffer resources
+// (base, byte count): loads past the end read zeros and stores past it are
+// dropped, so the lanes whose chunk lies past the row's end run the same
+// straight-line code as the others and need no branch or zeroing.
+constexpr int kLoadNonTemporal = 2;  // the cache-policy bit load_x16 sets
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <int POLICY>
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4i t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY);
+  return make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
+}
+__device__ __forceinline__ float4 bload16f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const uint4 u = bload16<0>(r, off);
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+__device__ __forceinline__ void bstore8(uint2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)v.x, (int)v.y}, r, (int)off, 0, 0);
+}
+
 // x~ codes of 8 values: Clip(Round(v * s), -128, 127) as bytes.  The product
 // is rounded to float, then 1.5 * 2^23 is added: the sum's unit in the last
 // place is 1, so the addition rounds v * s to the nearest integer, ties to
@@ -52,7 +74,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
                                                         int8_t* __restrict__ xq,
                                                         float* __restrict__ beta) {
   const int lane = lane_id();
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (t >= tokens) return;
   const int64_t nchunks = cols >> 3;
   const uint4* src = reinterpret_cast<const uint4*>(x + t * cols);
@@ -79,21 +101,21 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   us2 mh = {0, 0};
   uint32_t m;
   if constexpr (CPL > 0) {
+    // chunks past the row's end read as zeros (no effect on the max) and
+    // their codes are dropped by the store's range check
+    const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + t * cols, 2 * cols);
+    const __amdgpu_buffer_rsrc_t rq = row_rsrc(xq + t * cols, cols);
     uint4 v[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int64_t idx = lane + (int64_t)kWave * c;
-      v[c] = idx < nchunks ? load_x16(src, idx) : make_uint4(0u, 0u, 0u, 0u);
+      v[c] = bload16<kLoadNonTemporal>(rx, 16u * (uint32_t)(lane + kWave * c));
       mh = chunk_max(v[c], mh);
     }
     m = wave_max_dpp(fold(mh));
     const float b = fmaxf(__uint_as_float(m << 16), 1e-5f);
     const float s = __fdiv_rn(127.0f, b);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int64_t idx = lane + (int64_t)kWave * c;
-      if (idx < nchunks) dst[idx] = quant8(v[c], s);
-    }
+    for (int c = 0; c < CPL; ++c) bstore8(quant8(v[c], s), rq, 8u * (uint32_t)(lane + kWave * c));
     if (lane == 0) beta[t] = b;
   } else {
     for (int64_t base = 0; base < nchunks; base += kWave) {
@@ -133,7 +155,7 @@ __global__ __launch_bounds__(256) void rmsnorm_act_quant_kernel(const uint16_t* 
                                                                 int8_t* __restrict__ xq,
                                                                 float* __restrict__ beta) {
   const int lane = lane_id();
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (t >= tokens) return;
   const int64_t nchunks = cols >> 3;
   const uint4* src = reinterpret_cast<const uint4*>(x + t * cols);
@@ -148,12 +170,14 @@ __global__ __launch_bounds__(256) void rmsnorm_act_quant_kernel(const uint16_t* 
     }
   };
   // exact squares in double (a float square can overflow or lose bits),
-  // even and odd elements summed in two chains
+  // even and odd elements summed in two chains; a bf16 square has at most
+  // 16 significant bits and stays in double's normal range, so the fused
+  // multiply-add rounds exactly as the separate add of the exact product
   auto chunk_ss = [&](const uint4& d, double (&s)[2]) {
     float f[8];
     widen(d, f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e & 1] += (double)f[e] * (double)f[e];
+    for (int e = 0; e < 8; ++e) s[e & 1] = __builtin_fma((double)f[e], (double)f[e], s[e & 1]);
   };
   auto normalise = [&](const uint4& d, int64_t idx, float r, float (&n)[8]) {
     float f[8];
@@ -186,43 +210,53 @@ __global__ __launch_bounds__(256) void rmsnorm_act_quant_kernel(const uint16_t* 
   if constexpr (CPL > 0) {
     // With at most two chunks per lane, the lane's weights are requested
     // together with its x chunks (a longer row would hold too many
-    // registers: 183 instead of 122 VGPRs at ten chunks).
+    // registers: 183 instead of 122 VGPRs at ten chunks).  Chunks past the
+    // row's end read x = 0 and w = 0: their squares add nothing, their n is
+    // 0 or NaN (0 * r with r = inf), neither of which moves the float max
+    // of magnitudes, and their codes are dropped by the store's range check.
     constexpr bool kEarlyW = CPL <= 2;
+    const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + t * cols, 2 * cols);
+    const __amdgpu_buffer_rsrc_t rw = row_rsrc(w, 4 * cols);
+    const __amdgpu_buffer_rsrc_t rq = row_rsrc(xq + t * cols, cols);
     uint4 v[CPL];
     float4 wl[kEarlyW ? CPL : 1][2];
     double ss[2] = {0.0, 0.0};
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int64_t idx = lane + (int64_t)kWave * c;
-      const bool in = idx < nchunks;
-      v[c] = in ? load_x16(src, idx) : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t idx = (uint32_t)(lane + kWave * c);
+      v[c] = bload16<kLoadNonTemporal>(rx, 16u * idx);
       if constexpr (kEarlyW) {
-        wl[c][0] = in ? wsrc[2 * idx] : make_float4(0.f, 0.f, 0.f, 0.f);
-        wl[c][1] = in ? wsrc[2 * idx + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        wl[c][0] = bload16f(rw, 32u * idx);
+        wl[c][1] = bload16f(rw, 32u * idx + 16u);
       }
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) chunk_ss(v[c], ss);
     const float r = inv_rms(wave_sum_dpp(ss[0] + ss[1]));
+    // Longer rows request their weights only now, in two halves: hoisted
+    // above the reduction, or all at once, they would hold their registers
+    // alongside x (at ten chunks 133 VGPRs, three waves per SIMD, instead
+    // of 128 and four).
+    if constexpr (!kEarlyW) __builtin_amdgcn_sched_barrier(0);
     float n[CPL][8];
     float mf = 0.f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int64_t idx = lane + (int64_t)kWave * c;
-      if (idx < nchunks) {
-        if constexpr (kEarlyW) normalise_w(v[c], wl[c], r, n[c]);
-        else normalise(v[c], idx, r, n[c]);
-        mf = nmax(n[c], mf);
+      const uint32_t idx = (uint32_t)(lane + kWave * c);
+      if constexpr (kEarlyW) {
+        normalise_w(v[c], wl[c], r, n[c]);
+      } else {
+        if (c == CPL / 2) __builtin_amdgcn_sched_barrier(0);
+        const float4 wq[2] = {bload16f(rw, 32u * idx), bload16f(rw, 32u * idx + 16u)};
+        normalise_w(v[c], wq, r, n[c]);
       }
+      mf = nmax(n[c], mf);
     }
     const uint32_t m = wave_max_dpp(__float_as_uint(mf));
     const float b = fmaxf(__uint_as_float(m), 1e-5f);
     const float s = __fdiv_rn(127.0f, b);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int64_t idx = lane + (int64_t)kWave * c;
-      if (idx < nchunks) dst[idx] = quant8(n[c], s);
-    }
+    for (int c = 0; c < CPL; ++c) bstore8(quant8(n[c], s), rq, 8u * (uint32_t)(lane + kWave * c));
     if (lane == 0) beta[t] = b;
   } else {
     double ss[2] = {0.0, 0.0};

@@ -20,10 +20,17 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
+// The exchanges above stay within 16-lane rows and every lane is enabled,
+// so no lane keeps its old value: the 64-bit form leaves the old operand
+// undefined, which spares the zeroing moves of the destination halves.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32_nold(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+  const uint32_t lo = dpp_u32_nold<CTRL>((uint32_t)b), hi = dpp_u32_nold<CTRL>((uint32_t)(b >> 32));
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 __device__ __forceinline__ double readlane_f64(double v, int l) {
