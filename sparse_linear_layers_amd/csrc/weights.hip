@@ -57,6 +57,11 @@ __global__ __launch_bounds__(256) void nm_mask_kernel(const float* __restrict__ 
 //   MODE 0: mask read from mask_in (or none when mask_in is null)
 //   MODE 1: mask computed here, m = 4 (one chunk = one group)
 //   MODE 2: mask computed here, m = 8 (a group spans lanes 2i and 2i+1)
+//   MODE 3, 4: as MODE 1 for n = 3 and n = 2 (the common ratios), with the
+//           keep decisions as lane masks (quant_pack_row_m4); each has its
+//           own kernels, so the registers of one do not burden the others.
+// kMaskMode maps MODE 3 and 4 back to 1 where only the mask rule matters.
+template <int MODE> constexpr int kMaskMode = MODE >= 3 ? 1 : MODE;
 // CPL = 4-column chunks per lane held in registers; cols <= 256 * CPL.
 // ---------------------------------------------------------------------------
 struct RowJob {
@@ -80,14 +85,164 @@ __device__ __forceinline__ float4 load_w4_stream(const float4* p, int64_t idx) {
   return make_float4(t.x, t.y, t.z, t.w);
 }
 
+// Buffer resource over a row's bytes: loads past the end read zeros and
+// stores past it are dropped (rows here are at most 256 KB).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wrow_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kWLoadNonTemporal = 2;  // the cache-policy bit load_w4_stream sets
+
+typedef unsigned long long lanemask;  // one bit per lane of the wave
+__device__ __forceinline__ lanemask lanes(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+__device__ __forceinline__ bool mine(lanemask m) { return __builtin_amdgcn_inverse_ballot_w64(m); }
+
+// Dropped elements of each lane's group of four (m = 4), as lane masks, by
+// the rank rule of keep_mask<4>: for i < j, i beats j iff key_i >= key_j,
+// and otherwise j beats i, so six compares decide all twelve pairs.  An
+// element is dropped iff at least NK of the other three beat it (NK = 2 or
+// 3); the count is boolean logic on the compare masks, which live in scalar
+// registers and keep that work off the vector ALU.
+template <int NK>
+__device__ __forceinline__ void drop4(const float4& v, lanemask (&d)[4]) {
+  static_assert(NK == 2 || NK == 3, "the n = 2 and n = 3 rules");
+  const uint32_t k0 = abs_key(v.x), k1 = abs_key(v.y), k2 = abs_key(v.z), k3 = abs_key(v.w);
+  const lanemask c01 = lanes(k0 >= k1), c02 = lanes(k0 >= k2), c03 = lanes(k0 >= k3);
+  const lanemask c12 = lanes(k1 >= k2), c13 = lanes(k1 >= k3), c23 = lanes(k2 >= k3);
+  // the three "beaten by" masks of each element
+  const lanemask a[4] = {~c01, c01, c02, c03}, b[4] = {~c02, ~c12, c12, c13};
+  const lanemask c[4] = {~c03, ~c13, ~c23, c23};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (NK == 3)
+      d[j] = a[j] & b[j] & c[j];  // beaten by all three
+    else
+      d[j] = (a[j] & b[j]) | (c[j] & (a[j] | b[j]));  // by at least two
+  }
+}
+
+// The row kernel for an n:4 mask computed in the same pass, laid out like
+// quant_pack_row below but with every lane running the same straight-line
+// code: chunks past the row's end read zeros through the buffer resource
+// (they add nothing to the sum) and their stores fall outside it.  Keep
+// decisions are lane masks, recomputed from the loaded values in each loop
+// that needs them rather than held across the row.
+template <int CPL, bool BLOCK, int NK>
+__device__ __forceinline__ void quant_pack_row_m4(const RowJob& job, int64_t row_in,
+                                                 bool from_masked) {
+  // the row is the same for the whole wave: scalar registers (the buffer
+  // resources below must be)
+  const int64_t row = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(row_in >> 32)) << 32) |
+                                (uint32_t)__builtin_amdgcn_readfirstlane((int)row_in));
+  constexpr int NTH = BLOCK ? 256 : kWave;
+  const int lane = lane_id();
+  const int tid = BLOCK ? (int)threadIdx.x : lane;
+  const int64_t cols = job.cols;
+  const __amdgpu_buffer_rsrc_t rw = wrow_rsrc(job.W + row * cols, 4 * cols);
+  float4 v[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v t = __builtin_bit_cast(
+        f4v, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(16u * (uint32_t)(tid + NTH * c)), 0,
+                                                   kWLoadNonTemporal));
+    v[c] = make_float4(t.x, t.y, t.z, t.w);
+  }
+  // Each loop takes its own copy of a chunk through an empty asm statement,
+  // so the compiler neither merges the two loops' mask computations nor
+  // hoists them: their lane masks would overflow the scalar registers.
+  auto chunk = [&](int c) {
+    float4 x = v[c];
+    __asm__ volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+    return x;
+  };
+  // ---- scale: sum of |w| in double, lane partials then DPP exchanges ----
+  // (a dropped element adds +0.0, which leaves the sum as skipping it would)
+  float g;
+  if (job.scale_in) {
+    g = job.scale_in[row];
+  } else {
+    double s = 0.0;
+    if (from_masked) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float4 x = chunk(c);
+        lanemask d[4];
+        drop4<NK>(x, d);
+        const float a[4] = {fabsf(x.x), fabsf(x.y), fabsf(x.z), fabsf(x.w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += (double)(mine(d[e]) ? 0.f : a[e]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float a[4] = {fabsf(v[c].x), fabsf(v[c].y), fabsf(v[c].z), fabsf(v[c].w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += (double)a[e];
+      }
+    }
+    s = wave_sum_dpp(s);
+    if constexpr (BLOCK) {
+      __shared__ double red[4];
+      if (lane == 0) red[threadIdx.x >> 6] = s;
+      __syncthreads();
+      s = (red[0] + red[1]) + (red[2] + red[3]);
+    }
+    g = fmaxf((float)(s / (double)cols), 1e-5f);
+  }
+  // Clip(Round(w/g), -1, 1) is +-1 exactly when |w| > g/2 (g/2 is exact for
+  // g >= 1e-5, and w/g rounded to float exceeds 1/2 iff |w| > g/2): code 01
+  // for +1 and 10 for -1.
+  const float thr = g * 0.5f;
+  // ---- codes, packed 4 per byte; 4 lanes' bytes form one dword store ----
+  const __amdgpu_buffer_rsrc_t rp = wrow_rsrc(job.packed + row * (cols >> 2), cols >> 2);
+  const __amdgpu_buffer_rsrc_t rm = wrow_rsrc(job.mask_out + ((row * cols) >> 3), cols >> 3);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const uint32_t idx = (uint32_t)(tid + NTH * c);
+    const float4 x = chunk(c);
+    const float w[4] = {x.x, x.y, x.z, x.w};
+    lanemask d[4];
+    drop4<NK>(x, d);
+    uint32_t byte = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const lanemask nz = lanes(fabsf(w[e]) > thr) & ~d[e];
+      const lanemask neg = lanes((int)__float_as_uint(w[e]) < 0);
+      byte |= mine(nz & ~neg) ? (1u << (2 * e)) : 0u;
+      byte |= mine(nz & neg) ? (2u << (2 * e)) : 0u;
+    }
+    uint32_t word = byte << (8 * (lane & 3));
+    word |= dpp_u32<kDppXor1>(word);
+    word |= dpp_u32<kDppXor2>(word);
+    if ((lane & 3) == 0) __builtin_amdgcn_raw_buffer_store_b32(word, rp, (int)idx, 0, 0);
+    if (job.mask_out) {
+      uint32_t k4 = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) k4 |= mine(d[e]) ? 0u : (1u << e);
+      uint32_t mw = k4 << (4 * (lane & 7));
+      mw |= dpp_u32<kDppXor1>(mw);
+      mw |= dpp_u32<kDppXor2>(mw);
+      mw |= dpp_u32<kDppHalfMirror>(mw);  // the other quad of the 8 lanes
+      if ((lane & 7) == 0) __builtin_amdgcn_raw_buffer_store_b32(mw, rm, (int)(idx >> 1), 0, 0);
+    }
+    // one chunk's lane masks at a time (scalar registers run short otherwise)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (tid == 0) {
+    job.scale[row] = g;
+    if (job.scale_bf16) job.scale_bf16[row] = f32_to_bf16_rne(g);
+  }
+}
+
 // One row per wave (BLOCK = false), or per block of 256 threads for long rows
 // (BLOCK = true: the four waves' double sums meet in LDS in a fixed order).
 // Chunk idx = thread + threads * c, so the chunks of a wave are consecutive
 // and the lane exchanges below (n:8 groups, code and mask packing) stay
 // inside a wave.
 template <int CPL, int MODE, bool BLOCK>
-__device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, int n,
-                                               bool from_masked) {
+__device__ __forceinline__ void quant_pack_row_bits(const RowJob& job, int64_t row, int n,
+                                                    bool from_masked) {
   constexpr int NTH = BLOCK ? 256 : kWave;
   const int lane = lane_id();
   const int tid = BLOCK ? (int)threadIdx.x : lane;
@@ -190,6 +345,17 @@ __device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, i
   }
 }
 
+template <int CPL, int MODE, bool BLOCK>
+__device__ __forceinline__ void quant_pack_row(const RowJob& job, int64_t row, int n,
+                                               bool from_masked) {
+  if constexpr (MODE == 3)
+    quant_pack_row_m4<CPL, BLOCK, 3>(job, row, from_masked);
+  else if constexpr (MODE == 4)
+    quant_pack_row_m4<CPL, BLOCK, 2>(job, row, from_masked);
+  else
+    quant_pack_row_bits<CPL, MODE, BLOCK>(job, row, n, from_masked);
+}
+
 // Rows longer than 256*32 columns: two passes over the row (the second
 // read is expected to hit L2), same arithmetic.
 template <int MODE>
@@ -274,7 +440,7 @@ template <int CPL, int MODE>
 __device__ __forceinline__ void quant_pack_dispatch(const RowJob& job, int64_t row, int n,
                                                     bool from_masked) {
   if constexpr (CPL == 0)
-    quant_pack_row_long<MODE>(job, row, n, from_masked);
+    quant_pack_row_long<kMaskMode<MODE>>(job, row, n, from_masked);
   else
     quant_pack_row<CPL, MODE, false>(job, row, n, from_masked);
 }
@@ -567,10 +733,17 @@ static void launch_row(int cpl, dim3 grid, hipStream_t stream, const RowJob& job
                        from_masked);                                                       \
     break;
     SBL_CASE(1) SBL_CASE(2) SBL_CASE(4) SBL_CASE(8) SBL_CASE(12) SBL_CASE(16) SBL_CASE(20)
-    SBL_CASE(24) SBL_CASE(28) SBL_CASE(32) SBL_CASE(0)
+    SBL_CASE(24) SBL_CASE(28) SBL_CASE(32)
 #undef SBL_CASE
+    case 0:  // the two-pass long-row path has no lane-mask variant
+      hipLaunchKernelGGL((quant_pack_kernel<0, kMaskMode<MODE>>), grid, dim3(256), 0, stream, job, n,
+                         from_masked);
+      break;
   }
 }
+
+// Mode of a row kernel with the mask computed in it (fuse_mask).
+static int fused_mode(int n, int m) { return m == 8 ? 2 : n == 3 ? 3 : n == 2 ? 4 : 1; }
 
 hipError_t launch_quant_pack(const float* W, const uint8_t* mask_in, int64_t rows, int64_t cols,
                              int n, int m, int fuse_mask, unsigned flags, uint8_t* mask_out,
@@ -590,12 +763,13 @@ hipError_t launch_quant_pack(const float* W, const uint8_t* mask_in, int64_t row
     hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(256), 0, stream, job);
     job.scale_in = scale;
   }
-  if (!fuse_mask)
-    launch_row<0>(cpl, grid, stream, job, n, fm);
-  else if (m == 4)
-    launch_row<1>(cpl, grid, stream, job, n, fm);
-  else
-    launch_row<2>(cpl, grid, stream, job, n, fm);
+  switch (fuse_mask ? fused_mode(n, m) : 0) {
+    case 0: launch_row<0>(cpl, grid, stream, job, n, fm); break;
+    case 1: launch_row<1>(cpl, grid, stream, job, n, fm); break;
+    case 2: launch_row<2>(cpl, grid, stream, job, n, fm); break;
+    case 3: launch_row<3>(cpl, grid, stream, job, n, fm); break;
+    default: launch_row<4>(cpl, grid, stream, job, n, fm); break;
+  }
   return hipGetLastError();
 }
 
@@ -609,8 +783,12 @@ static void launch_grouped(int cpl, dim3 grid, hipStream_t stream, const Grouped
                        fm);                                                                      \
     break;
     SBL_CASE(1) SBL_CASE(2) SBL_CASE(4) SBL_CASE(8) SBL_CASE(12) SBL_CASE(16) SBL_CASE(20)
-    SBL_CASE(24) SBL_CASE(28) SBL_CASE(32) SBL_CASE(0)
+    SBL_CASE(24) SBL_CASE(28) SBL_CASE(32)
 #undef SBL_CASE
+    case 0:
+      hipLaunchKernelGGL((quant_pack_grouped_kernel<0, kMaskMode<MODE>>), grid, dim3(256), 0, stream,
+                         a, n, fm);
+      break;
   }
 }
 
@@ -690,10 +868,12 @@ hipError_t launch_quant_pack_grouped(const sbl_refresh_desc* host, const sbl_ref
       a.block_start[cnt] = (int)blocks;
       if (blocks > 0) {
         const dim3 grid((unsigned)blocks);
-        if (m == 4)
-          launch_grouped<1>(cls, grid, stream, a, n, fm);
-        else
-          launch_grouped<2>(cls, grid, stream, a, n, fm);
+        switch (fused_mode(n, m)) {
+          case 1: launch_grouped<1>(cls, grid, stream, a, n, fm); break;
+          case 2: launch_grouped<2>(cls, grid, stream, a, n, fm); break;
+          case 3: launch_grouped<3>(cls, grid, stream, a, n, fm); break;
+          default: launch_grouped<4>(cls, grid, stream, a, n, fm); break;
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
       }

@@ -119,6 +119,20 @@ def test_nm_mask_quant_pack_fused(sbl, n, m, rows, cols, flags):
     _check_quant(W, mask, flags, packed, scale, sb)
 
 
+@pytest.mark.parametrize("n", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("rows,cols", [(24, 896), (5, 7168)])
+@pytest.mark.parametrize("flags", [0, 1])
+def test_nm_mask_quant_pack_fused_every_n4(sbl, n, rows, cols, flags):
+    """Every n of 4 on rows full of equal magnitudes and signed zeros, where
+    the rank rule's tie-break decides: n = 3 and 2 run the kernels that keep
+    their decisions as lane masks, the other n the kernel that keeps bits."""
+    W = tie_heavy(f"gpu/fused_ties/{n}/{rows}x{cols}", rows, cols)
+    mask_d, packed, scale, sb = sbl.nm_mask_quant_pack(dev(W), n, 4, flags)
+    mask = oracle.nm_mask(W, n, 4)
+    assert np.array_equal(host(mask_d), mask)
+    _check_quant(W, mask, flags, packed, scale, sb)
+
+
 def test_quant_edge_rows(sbl):
     W = synth.latent_weight("gpu/quant/edge", 6, 256)
     W[0] = 0.0                       # all-zero row: gamma clamps to 1e-5
@@ -179,7 +193,7 @@ def test_grouped_refresh(sbl):
 
 
 
-@pytest.mark.parametrize("n,m,flags", [(3, 4, 0), (6, 8, 0), (3, 4, 1), (4, 8, 1)])
+@pytest.mark.parametrize("n,m,flags", [(3, 4, 0), (6, 8, 0), (3, 4, 1), (4, 8, 1), (2, 4, 1), (1, 4, 0)])
 def test_grouped_refresh_mixed_row_classes(sbl, n, m, flags):
     """One grouped call over rows of every footprint: short rows (a wave
     each), rows of 2049..32768 columns (a block each, in one launch with the
