@@ -49,7 +49,8 @@ struct GemmArgs {
   int scale_bf16;
   int vec_store;  // N % 4 == 0: 16-byte stores
   int tiles_o;
-  int ntiles;
+  int ntiles;  // whole tiles
+  int nhalf;   // warp-specialised kernel: half tiles (along t) after the whole ones
 };
 
 // Tiles of hardware block b in a grid of G blocks: the tiles are cut into
@@ -393,9 +394,30 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void gemm_i8_ws_kernel(Ge
   const int kbytes = (int)(K >> 2);
   const int KT = (int)((K + BK - 1) / BK);
 
+  // This block's work items: its whole tiles, then its half tile, if any
+  // (the last tiles of the problem cut in two along t, so that the grid's
+  // last round costs half a tile: at most one per block).
   const TileRange tr = tile_range(blockIdx.x, gridDim.x, a.ntiles);
-  if (tr.first >= tr.end) return;
-  const int total = ((tr.end - tr.first + tr.step - 1) / tr.step) * KT;
+  const TileRange th = tile_range(blockIdx.x, gridDim.x, a.nhalf);
+  const int nfull = tr.first < tr.end ? (tr.end - tr.first + tr.step - 1) / tr.step : 0;
+  const int items = nfull + (th.first < th.end ? (th.end - th.first + th.step - 1) / th.step : 0);
+  if (items == 0) return;
+  const int total = items * KT;
+  // item -> first feature, first token and token rows (0 for the empty
+  // second half of a ragged last tile row)
+  auto geom = [&](int item, int64_t& o0, int64_t& t0, int64_t& rows) {
+    int tile, half = -1;
+    if (item < nfull) {
+      tile = tr.first + item * tr.step;
+    } else {
+      const int h = th.first + (item - nfull) * th.step;
+      tile = a.ntiles + (h >> 1);
+      half = h & 1;
+    }
+    o0 = (int64_t)(tile % a.tiles_o) * BO;
+    t0 = (int64_t)(tile / a.tiles_o) * BT + (half > 0 ? BT / 2 : 0);
+    rows = max((int64_t)0, min((int64_t)(half < 0 ? BT : BT / 2), T - t0));
+  };
   const int total2 = (total + 1) & ~1;  // both roles pass the same (even) number of barriers
 
   if (wave < MATH) {
@@ -409,10 +431,9 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void gemm_i8_ws_kernel(Ge
 
     // y = ((float)acc * beta/127) * gamma, one dword per register: lanes
     // 0-31 and 32-63 each write 128 contiguous bytes of one token row
-    auto epilogue = [&](int tile, int par) {
-      const int64_t o0 = (int64_t)(tile % a.tiles_o) * BO;
-      const int64_t t0 = (int64_t)(tile / a.tiles_o) * BT;
-      const int64_t rows_t = min((int64_t)BT, T - t0);
+    auto epilogue = [&](int item, int par) {
+      int64_t o0, t0, rows_t;
+      geom(item, o0, t0, rows_t);
       const int N4 = (int)N * 4;
       const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(a.y + t0 * N, rows_t * N * 4);
       const int ol = wo * WO + (lane & 31);
@@ -466,10 +487,12 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void gemm_i8_ws_kernel(Ge
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = v16i{};
     };
-    int tile = tr.first, kt = 0, par = 0;
+    int item = 0, kt = 0, par = 0;
+    // on a half tile the waves of the second 128 tokens have nothing to do
+    bool idle = nfull == 0 && wt * WT >= BT / 2;
     __syncthreads();  // step 0 staged
     for (int s = 0; s < total2; ++s) {
-      if (s < total) {
+      if (s < total && !idle) {
         const int buf = s & 1;
         // k order inside a step: lane half h takes k in [64h, 64h + 64), and
         // for product kk its 16 values [64h + 16kk, +16), in the byte order
@@ -514,12 +537,14 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void gemm_i8_ws_kernel(Ge
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        if (++kt == KT) {
-          epilogue(tile, par);
-          kt = 0;
-          tile += tr.step;
-          par ^= 1;
-        }
+      }
+      if (s < total && ++kt == KT) {
+        // (an idle wave's stores lie past the half tile's rows: dropped)
+        epilogue(item, par);
+        kt = 0;
+        ++item;
+        par ^= 1;
+        idle = item >= nfull && wt * WT >= BT / 2;
       }
       __syncthreads();
     }
@@ -539,18 +564,18 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void gemm_i8_ws_kernel(Ge
     uint8_t* const wdst = &sW[0][lt * WSTRIDE];
     int8_t* const xdst = &sX[0][x_row * STRIDE + x_part];
 
-    int ld_tile = tr.first, ld_kt = 0, ld_par = 0;
+    int ld_item = 0, ld_kt = 0, ld_par = 0;
     int64_t ld_o0 = 0, ld_t0 = 0;
     __amdgpu_buffer_rsrc_t rc, rx, rg, rb;
     constexpr int GB = SCALE_BF16 ? 2 : 4;  // bytes per row scale
     auto rebase = [&]() {
-      ld_o0 = (int64_t)(ld_tile % a.tiles_o) * BO;
-      ld_t0 = (int64_t)(ld_tile / a.tiles_o) * BT;
+      int64_t rows_t;
+      geom(ld_item, ld_o0, ld_t0, rows_t);
       rc = buffer_rsrc(a.packed + ld_o0 * kbytes, min((int64_t)BO, N - ld_o0) * kbytes);
-      rx = buffer_rsrc(a.xq + ld_t0 * K, min((int64_t)BT, T - ld_t0) * K);
+      rx = buffer_rsrc(a.xq + ld_t0 * K, rows_t * K);
       // the tile's row scales and beta: entries past N or T read as zero
       rg = buffer_rsrc(static_cast<const char*>(a.scale) + ld_o0 * GB, min((int64_t)BO, N - ld_o0) * GB);
-      rb = buffer_rsrc(a.beta + ld_t0, min((int64_t)BT, T - ld_t0) * 4);
+      rb = buffer_rsrc(a.beta + ld_t0, rows_t * 4);
     };
     rebase();
 
@@ -575,9 +600,9 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void gemm_i8_ws_kernel(Ge
     _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                   \
       b##S[nb] = __builtin_amdgcn_raw_buffer_load_b32(rb, (lt + nb * LT) * 4, 0, 0);    \
     if (++ld_kt == KT) {                                                                \
-      if (ld_tile + tr.step < tr.end) {                                                 \
+      if (ld_item + 1 < items) {                                                        \
         ld_kt = 0;                                                                      \
-        ld_tile += tr.step;                                                             \
+        ++ld_item;                                                                      \
         ld_par ^= 1;                                                                    \
         rebase();                                                                       \
       } else {                                                                          \
@@ -661,8 +686,22 @@ hipError_t launch_gemm(const int8_t* xq, const float* beta, const uint8_t* packe
   // rows of y and x~
   if (ws_o * ws_t >= slots && (int64_t)C::BT * N * 4 < INT32_MAX / 2) {
     a.tiles_o = (int)ws_o;
-    a.ntiles = (int)(ws_o * ws_t);
-    const int grid = (int)std::min<int64_t>(a.ntiles, slots);
+    const int64_t tiles = ws_o * ws_t;
+    // When the last round of tiles fills at most half the grid, an
+    // HBM-bound product runs it as twice as many half tiles, one per block,
+    // instead of whole tiles on half the blocks: a half tile stores half the
+    // bytes (measured 7% faster on a 1152 x 896 product at 32768 tokens).
+    // A product bound by the matrix cores keeps whole tiles: its tile time is
+    // set per wave, and a half tile leaves each SIMD one math wave, which
+    // takes about as long as two.  The bound is the product's intensity
+    // against the ridge of 5 int8 POP/s over 8 TB/s (625 ops per byte).
+    const int64_t rem = tiles % slots;
+    const double ops = 2.0 * (double)T * (double)N * (double)K;
+    const double bytes = (double)T * K + (double)N * K / 4 + 4.0 * N + 4.0 * T + 4.0 * T * N;
+    const bool hbm_bound = ops < 625.0 * bytes;
+    a.nhalf = (hbm_bound && rem > 0 && 2 * rem <= slots) ? (int)(2 * rem) : 0;
+    a.ntiles = (int)(tiles - a.nhalf / 2);
+    const int grid = (int)std::min<int64_t>(tiles, slots);
     if (scale_bf16)
       hipLaunchKernelGGL((gemm_i8_ws_kernel<C, true>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
     else
