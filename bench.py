@@ -600,12 +600,17 @@ def secondary(torch, sbl, synth, dev, timer, flush):
         wn = torch.from_numpy(synth.norm_weight(f"cfg2/rms/w/{K}", K)).to(dev)
         xq_o = torch.empty((T, K), dtype=torch.int8, device=dev)
         b_o = torch.empty(T, dtype=torch.float32, device=dev)
-        ur = graph_time(torch, [lambda: sbl.rmsnorm_act_quant_i8(xb, wn, 1e-6, xq_o, b_o)], reps=30)
-        ua = graph_time(torch, [lambda: sbl.act_quant_i8(xb, xq_o, b_o)], reps=30)
+        # timed as the products are (events around each launch, queued behind
+        # a flush, so from HBM and without a graph launch per call); the
+        # replayed-graph figure, which adds a launch per replay, beside it
+        _, ur = timer.time(lambda i=0: sbl.rmsnorm_act_quant_i8(xb, wn, 1e-6, xq_o, b_o), 20, flush=flush)
+        _, ua = timer.time(lambda i=0: sbl.act_quant_i8(xb, xq_o, b_o), 20, flush=flush)
+        ur, ua = ur * 1e3, ua * 1e3
+        urg = graph_time(torch, [lambda: sbl.rmsnorm_act_quant_i8(xb, wn, 1e-6, xq_o, b_o)], reps=30)
         byts = 3.0 * T * K + 4 * T
         rms[f"K{K}"] = {"us": round(ur, 2), "gbs": round(byts / (ur * 1e-6) / 1e9, 1),
                         "frac_hbm": round(byts / (ur * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                        "act_quant_alone_us": round(ua, 2)}
+                        "act_quant_alone_us": round(ua, 2), "us_graph_replay": round(urg, 2)}
         del xb, xq_o
     nxt["rmsnorm_act_quant_T32768"] = rms
     # mask monitor over a bandwidth-sized input: the 16 gate masks of the
@@ -618,7 +623,7 @@ def secondary(torch, sbl, synth, dev, timer, flush):
     mb = sbl.nm_mask_create(Wm, 3, 4)
     del Wm
     st = torch.empty(2, dtype=torch.int64, device=dev)
-    _, mm = timer.time(lambda i=0: sbl.nm_mask_stats(ma, mb, rows_m, cols_m, 3, 4, st), 20)
+    _, mm = timer.time(lambda i=0: sbl.nm_mask_stats(ma, mb, rows_m, cols_m, 3, 4, st), 20, flush=flush)
     mbytes = 2.0 * rows_m * cols_m / 8
     torch.cuda.synchronize()
     nxt["mask_stats_wide_gate_stack_3of4"] = {
@@ -630,12 +635,18 @@ def secondary(torch, sbl, synth, dev, timer, flush):
     # per-tensor absmean refresh of the gate matrix (reads W twice)
     Wg = torch.from_numpy(synth.latent_weight("cfg2/L0/gate/W", 4864, 896)).to(dev)
     outs = sbl.nm_mask_quant_pack(Wg, 3, 4, sbl.SCALE_PER_TENSOR, want_mask=False)
+    # three launches (row sums, the tensor scale, the codes): replayed as a
+    # graph, as a training loop launches a refresh, and by events after a
+    # flush beside it
     up = graph_time(torch, [lambda: sbl.nm_mask_quant_pack(Wg, 3, 4, sbl.SCALE_PER_TENSOR, out=outs)], reps=50)
     uq = graph_time(torch, [lambda: sbl.nm_mask_quant_pack(Wg, 3, 4, 0, out=outs)], reps=50)
+    _, upc = timer.time(lambda i=0: sbl.nm_mask_quant_pack(Wg, 3, 4, sbl.SCALE_PER_TENSOR, out=outs), 20,
+                        flush=flush)
     nw = 4864 * 896
     nxt["per_tensor_refresh_gate_4864x896"] = {
         "us": round(up, 2), "gbs": round(8.25 * nw / (up * 1e-6) / 1e9, 1),
-        "per_row_us": round(uq, 2), "per_row_gbs": round(4.25 * nw / (uq * 1e-6) / 1e9, 1)}
+        "per_row_us": round(uq, 2), "per_row_gbs": round(4.25 * nw / (uq * 1e-6) / 1e9, 1),
+        "us_cold_events": round(upc * 1e3, 2)}
     # straight-through backward of the gate and down linears at 32768
     # tokens: dx and dw separately (each is 2*T*N*K float products; the
     # matrix cores run three bf16 pieces of each)
