@@ -92,6 +92,14 @@ class Timer:
 
     def __init__(self, torch):
         self.torch = torch
+        self.last = None  # the last call's per-launch times, ms
+
+    def spread_us(self):
+        """median, 10th and 90th percentile of the last call's launches, us"""
+        ms = self.last
+        return {"us_median": round(float(np.median(ms)) * 1e3, 2),
+                "us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                "us_p90": round(float(np.percentile(ms, 90)) * 1e3, 2), "launches": int(len(ms))}
 
     def time(self, fn, iters, warmup=2, flush=None):
         torch = self.torch
@@ -111,6 +119,7 @@ class Timer:
             evs.append((a, b))
         torch.cuda.synchronize()
         ms = np.array([a.elapsed_time(b) for a, b in evs])
+        self.last = ms
         return float(np.median(ms)), float(np.mean(ms))
 
 
@@ -253,8 +262,12 @@ def main():
     per_shape = {}
     tot_ms, tot_ops, tot_bytes = 0.0, 0.0, 0.0
     for name, _, _, N, K in proj:
-        med, mean = timer.time(lambda i=0, nm=name: gemm(nm), 20, flush=flush)
+        med, mean = timer.time(lambda i=0, nm=name: gemm(nm), 50, flush=flush)
         per_shape[name] = product_rates(T, N, K, n, m, mean)
+        per_shape[name].update(timer.spread_us())
+        # warm (the inputs left in the Infinity Cache by the launch before),
+        # reported beside the cold figure that the rates use
+        per_shape[name]["us_warm"] = round(timer.time(lambda i=0, nm=name: gemm(nm), 20)[1] * 1e3, 2)
         tot_ms += mean
         tot_ops += 2.0 * T * N * K
         tot_bytes += per_shape[name]["bytes"]

@@ -463,13 +463,14 @@ def test_sparse24_full_size(sbl, name, N, K):
 
 @pytest.mark.parametrize("T,K,N,bf16_scale", [(16400, 320, 1000, False), (16400, 192, 1004, True),
                                                 (8292, 896, 4864, False), (16385, 4864, 896, True),
-                                                (16400, 192, 1002, False)])
+                                                (16400, 192, 1002, False), (8192, 448, 7100, True)])
 def test_sparse24_large_tiles(sbl, T, K, N, bf16_scale):
     """Sizes that take the large-tile smfmac kernel (at least one 256 x 256
     tile per CU, N % 4 == 0): ragged token and row edges, K % 128 == 64,
     bf16 row scales; N % 4 != 0 takes the small-tile kernel.  y equal to the
-    dense product's everywhere; acc and y of every token against the
-    oracle."""
+    dense product's everywhere (which runs its last round of tiles as half
+    tiles at the HBM-bound sizes here); acc and y of every token against
+    the oracle."""
     o = _operands(f"gpu/sp24_big/{T}x{K}x{N}", T, K, N, n=2, m=4)
     scale = dev(o["gb"]) if bf16_scale else dev(o["g"])
     bad = torch.zeros(1, dtype=torch.int32, device=DEV)
