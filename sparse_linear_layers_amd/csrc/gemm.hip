@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256, (BM * BN <= 128 * 128) ? 2 : 1) void gemm_i8_k
 //  * Loads and stores go through buffer resources rebased per tile; rows
 //    past N or T read as zero and their stores are dropped by the hardware
 //    range check.
-template <int BO_, int BT_, int MATH_, int LOADERS_, int BLOCKS_PER_CU_>
+template <int BO_, int BT_, int MATH_, int LOADERS_, int BLOCKS_PER_CU_, int WO_ = 64, int WT_ = 128>
 struct WsCfg {
   static constexpr int BO = BO_, BT = BT_, BK = 128;
   static constexpr int MATH = MATH_, LOADERS = LOADERS_;
@@ -334,7 +334,7 @@ struct WsCfg {
   static constexpr int WAVES_PER_SIMD = (NT / 64 * BLOCKS_PER_CU + 3) / 4;
   static constexpr int STRIDE = BK + 16;       // bytes per staged x~ row: 16-lane fragment reads hit all 64 banks once
   static constexpr int WSTRIDE = BK / 4 + 16;  // bytes per staged row of packed codes (same property)
-  static constexpr int WO = 64, WT = 128;      // math wave tile
+  static constexpr int WO = WO_, WT = WT_;     // math wave tile
   static constexpr int WAVES_O = BO / WO;      // math waves along o
   static constexpr int TI = WT / 32, TJ = WO / 32;
   static constexpr int CW = BK / 64;         // 16-byte code chunks per weight row and k step
@@ -354,6 +354,10 @@ struct WsCfg {
 // slower on the gate/up projection; so did starting half of the blocks
 // half a tile late.)
 using WsMain = WsCfg<256, 256, 8, 4, 1>;
+// Problems whose 256 x 256 tiles leave a partial last round can take
+// 256 x 128 tiles instead (8 math waves of 32 x 128: the same code-expansion
+// work per MFMA, twice the x~ fragment reads), in rounds of half the cost.
+using WsHalf = WsCfg<256, 128, 8, 4, 1, 32, 128>;
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0,
 // stores past it are dropped.  Callers keep every offset in the per-lane
@@ -673,20 +677,37 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The warp-specialised kernel on configuration C: tiles dealt to one block
+// per CU, the last half-full round as half tiles where that pays (below).
+template <class C>
+static hipError_t launch_ws(GemmArgs a, int64_t tiles_o, int64_t tiles_t, int64_t slots, bool halves,
+                            hipStream_t stream) {
+  a.tiles_o = (int)tiles_o;
+  const int64_t tiles = tiles_o * tiles_t;
+  const int64_t rem = tiles % slots;
+  a.nhalf = (halves && rem > 0 && 2 * rem <= slots) ? (int)(2 * rem) : 0;
+  a.ntiles = (int)(tiles - a.nhalf / 2);
+  const int grid = (int)std::min<int64_t>(tiles, slots);
+  if (a.scale_bf16)
+    hipLaunchKernelGGL((gemm_i8_ws_kernel<C, true>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_i8_ws_kernel<C, false>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const int8_t* xq, const float* beta, const uint8_t* packed,
                        const void* scale, int scale_bf16, int64_t T, int64_t K, int64_t N, float* y,
                        int32_t* acc, hipStream_t stream) {
-  using C = WsMain;
   GemmArgs a{xq, beta, packed, scale, y, acc, T, K, N, scale_bf16, (N % 4) == 0, 0, 0};
-  const int64_t ws_o = (N + C::BO - 1) / C::BO, ws_t = (T + C::BT - 1) / C::BT;
-  const int slots = device_cus(stream_device(stream)) * C::BLOCKS_PER_CU;
-  if (ws_o * ws_t > INT32_MAX || ((N + 127) / 128) * ((T + 127) / 128) > INT32_MAX)
+  const int64_t ws_o = (N + WsMain::BO - 1) / WsMain::BO, ws_t = (T + WsMain::BT - 1) / WsMain::BT;
+  const int64_t wh_t = (T + WsHalf::BT - 1) / WsHalf::BT;
+  const int64_t slots = device_cus(stream_device(stream));  // one block per CU in both layouts
+  if (ws_o * wh_t > INT32_MAX || ((N + 127) / 128) * ((T + 127) / 128) > INT32_MAX)
     return hipErrorInvalidValue;
   // the warp-specialised kernel keeps 32-bit buffer offsets within a tile's
   // rows of y and x~
-  if (ws_o * ws_t >= slots && (int64_t)C::BT * N * 4 < INT32_MAX / 2) {
-    a.tiles_o = (int)ws_o;
-    const int64_t tiles = ws_o * ws_t;
+  const bool offsets_ok = (int64_t)WsMain::BT * N * 4 < INT32_MAX / 2;
+  if (offsets_ok && ws_o * ws_t >= slots) {
     // When the last round of tiles fills at most half the grid, an
     // HBM-bound product runs it as twice as many half tiles, one per block,
     // instead of whole tiles on half the blocks: a half tile stores half the
@@ -695,19 +716,22 @@ hipError_t launch_gemm(const int8_t* xq, const float* beta, const uint8_t* packe
     // set per wave, and a half tile leaves each SIMD one math wave, which
     // takes about as long as two.  The bound is the product's intensity
     // against the ridge of 5 int8 POP/s over 8 TB/s (625 ops per byte).
-    const int64_t rem = tiles % slots;
     const double ops = 2.0 * (double)T * (double)N * (double)K;
     const double bytes = (double)T * K + (double)N * K / 4 + 4.0 * N + 4.0 * T + 4.0 * T * N;
     const bool hbm_bound = ops < 625.0 * bytes;
-    a.nhalf = (hbm_bound && rem > 0 && 2 * rem <= slots) ? (int)(2 * rem) : 0;
-    a.ntiles = (int)(tiles - a.nhalf / 2);
-    const int grid = (int)std::min<int64_t>(tiles, slots);
-    if (scale_bf16)
-      hipLaunchKernelGGL((gemm_i8_ws_kernel<C, true>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_i8_ws_kernel<C, false>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
-    return hipGetLastError();
+    // Rounds of whole tiles (a half-full last round at half cost where it
+    // runs as half tiles), against rounds of 256 x 128 tiles at 0.575 of a
+    // whole round each: at equal work the narrower tiles measured 5-12%
+    // slower (2048 x 2048 and 2048 x 7168 at 8192 tokens, one wide tile per
+    // CU), and 5-9% faster where they save a partial round (12288 tokens;
+    // a ragged last token row).
+    const int64_t full = ws_o * ws_t / slots, rem = ws_o * ws_t % slots;
+    const double main_rounds = (double)full + (rem == 0 ? 0.0 : (hbm_bound && 2 * rem <= slots) ? 0.5 : 1.0);
+    const double half_rounds = 0.575 * (double)((ws_o * wh_t + slots - 1) / slots);
+    if (half_rounds < main_rounds) return launch_ws<WsHalf>(a, ws_o, wh_t, slots, false, stream);
+    return launch_ws<WsMain>(a, ws_o, ws_t, slots, hbm_bound, stream);
   }
+  if (offsets_ok && ws_o * wh_t >= slots) return launch_ws<WsHalf>(a, ws_o, wh_t, slots, false, stream);
   return launch_cfg<128, 128, 2>(a, stream);
 }
 
