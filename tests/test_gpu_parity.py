@@ -311,13 +311,16 @@ def test_gemm_extreme_operands(sbl):
 
 @pytest.mark.parametrize("T,K,N,bf16_scale", [(16400, 320, 1000, False), (16400, 192, 1002, True),
                                                 (8292, 896, 4864, False), (16385, 4864, 896, True),
-                                                (8192, 448, 7100, False)])
+                                                (8192, 448, 7100, False), (100, 192, 65539, True),
+                                                (300, 320, 30001, False)])
 def test_gemm_large_tiles(sbl, T, K, N, bf16_scale):
-    """Sizes that take the large-tile persistent kernel (at least one tile
-    per CU): ragged token and row edges, K % 128 == 64, N % 4 != 0; acc and
-    y compared on every token.  Each shape's last round of tiles is run as
-    half tiles (on 256 CUs): over ragged last token rows (an empty second
-    half), and over whole ones with a ragged feature edge (8192 x 7100)."""
+    """Sizes that take the warp-specialised kernel (on 256 CUs): ragged
+    token and row edges, K % 128 == 64, N % 4 != 0; acc and y compared on
+    every token.  On 256 x 256 tiles the HBM-bound shapes run their last
+    round as half tiles, over ragged last token rows (an empty second half)
+    and over whole ones with a ragged feature edge (8192 x 7100); 16385 x
+    4864 x 896 and the few-token, many-feature shapes (one 100-token row;
+    128 + 128 + 44 tokens) take 256 x 128 tiles."""
     o = _operands(f"gpu/gemm_big/{T}x{K}x{N}", T, K, N)
     scale = dev(o["gb"]) if bf16_scale else dev(o["g"])
     y, acc = sbl.sparse_bitlinear_gemm(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), scale,
