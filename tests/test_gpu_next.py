@@ -249,3 +249,44 @@ def test_ste_backward_full_size_sampled(sbl, name, N, K):
     bdx, bdw = _ste_bounds(o, rows=rows, cols=cols)
     assert (np.abs(host(dx)[rows].astype(np.float64) - dx_ref) <= bdx).all()
     assert (np.abs(host(dw)[:, cols].astype(np.float64) - dw_ref) <= bdw).all()
+
+
+def test_ste_backward_single_term_reductions_are_exact(sbl):
+    """Reductions with one nonzero term at full length: codes with one +-1
+    per input column (dx sums 4864 output features), x~ with one +-1 per
+    input column (dw sums 32768 tokens).  Each result is then one exact
+    product (a float times +-1: the three bf16 pieces add back to it exactly
+    and every other term is zero), so dx and dw must equal the oracle's bit
+    for bit: a lost or mis-scaled bf16 piece, which the accumulation bound
+    at these lengths would not catch, changes the low bits."""
+    # dx: 1024 tokens, 4864 -> 896 (the gate linear's backward to its input)
+    T, N, K = 1024, 4864, 896
+    W = synth.latent_weight("gpu/ste1/W", N, K)
+    g, _ = oracle.row_scale(W)
+    codes = np.zeros((N, K), np.int8)
+    k = np.arange(K)
+    codes[(37 * k + 11) % N, k] = np.where(k % 3 == 0, -1, 1).astype(np.int8)
+    xq, beta = oracle.act_quant(synth.activations_bf16("gpu/ste1/x", T, K))
+    dy = synth.grad_output("gpu/ste1/dy", T, N)
+    dx, _ = sbl.sparse_bitlinear_ste_backward(dev(dy), dev(xq), dev(beta), dev(oracle.pack_codes(codes)),
+                                              dev(g), want_dw=False)
+    dx_ref, _ = oracle.ste_backward(dy, xq, beta, codes, g, want_dw=False)
+    assert np.array_equal(host(dx), dx_ref)
+    # dw: 32768 tokens, 64 output features, 896 input columns
+    T, N, K = synth.QWEN05B_PREFILL_TOKENS, 64, 896
+    W = synth.latent_weight("gpu/ste1w/W", N, K)
+    g, _ = oracle.row_scale(W)
+    codes = oracle.ternary_codes(W, oracle.nm_mask(W, 3, 4), g)
+    _, beta = oracle.act_quant(synth.activations_bf16("gpu/ste1w/x", T, K))
+    xq = np.zeros((T, K), np.int8)
+    k = np.arange(K)
+    xq[(7919 * k + 5) % T, k] = np.where(k % 2 == 0, 1, -1).astype(np.int8)
+    dy = synth.grad_output("gpu/ste1w/dy", T, N)
+    _, dw = sbl.sparse_bitlinear_ste_backward(dev(dy), dev(xq), dev(beta), dev(oracle.pack_codes(codes)),
+                                              dev(g), want_dx=False)
+    _, dw_ref = oracle.ste_backward(dy, xq, beta, codes, g, want_dx=False)
+    assert np.array_equal(host(dw), dw_ref)
+    # the pieces below the top bf16 one carry weight here: dropping them
+    # would move most results
+    top = (dw_ref.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    assert (top != dw_ref).mean() > 0.9
