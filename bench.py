@@ -613,18 +613,41 @@ def secondary(torch, sbl, synth, dev, timer, flush):
         wn = torch.from_numpy(synth.norm_weight(f"cfg2/rms/w/{K}", K)).to(dev)
         xq_o = torch.empty((T, K), dtype=torch.int8, device=dev)
         b_o = torch.empty(T, dtype=torch.float32, device=dev)
-        # timed as the products are (events around each launch, queued behind
-        # a flush, so from HBM and without a graph launch per call); the
-        # replayed-graph figure, which adds a launch per replay, beside it
-        _, ur = timer.time(lambda i=0: sbl.rmsnorm_act_quant_i8(xb, wn, 1e-6, xq_o, b_o), 20, flush=flush)
-        _, ua = timer.time(lambda i=0: sbl.act_quant_i8(xb, xq_o, b_o), 20, flush=flush)
-        ur, ua = ur * 1e3, ua * 1e3
+        # The headline figure streams: launches back to back over rotated
+        # copies of x and of the outputs (more than twice the Infinity Cache
+        # in all, so every launch reads from HBM), as a pipeline of layers
+        # launches this pass; per launch, the gap to the next included.
+        # Beside it: events around single launches queued behind a flush
+        # (which add the event and launch latency of one call, ~3 us), and
+        # replays of a one-launch graph.
+        rot = max(2, -(-2 * FLUSH_BYTES // int(3 * T * K)))
+        xs_r = [xb] + [xb.clone() for _ in range(rot - 1)]
+        outs_r = [(torch.empty((T, K), dtype=torch.int8, device=dev), torch.empty(T, dtype=torch.float32, device=dev))
+                  for _ in range(rot)]
+
+        def stream(fn, reps=6 * rot):
+            for i in range(rot):
+                fn(i)
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(reps):
+                fn(i % rot)
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / reps
+
+        ur = stream(lambda i: sbl.rmsnorm_act_quant_i8(xs_r[i], wn, 1e-6, outs_r[i][0], outs_r[i][1]))
+        ua = stream(lambda i: sbl.act_quant_i8(xs_r[i], outs_r[i][0], outs_r[i][1]))
+        _, ure = timer.time(lambda i=0: sbl.rmsnorm_act_quant_i8(xb, wn, 1e-6, xq_o, b_o), 20, flush=flush)
         urg = graph_time(torch, [lambda: sbl.rmsnorm_act_quant_i8(xb, wn, 1e-6, xq_o, b_o)], reps=30)
         byts = 3.0 * T * K + 4 * T
         rms[f"K{K}"] = {"us": round(ur, 2), "gbs": round(byts / (ur * 1e-6) / 1e9, 1),
                         "frac_hbm": round(byts / (ur * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                        "act_quant_alone_us": round(ua, 2), "us_graph_replay": round(urg, 2)}
-        del xb, xq_o
+                        "act_quant_alone_us": round(ua, 2), "rotated_copies": rot,
+                        "us_events_after_flush": round(ure * 1e3, 2), "us_graph_replay": round(urg, 2)}
+        del xb, xq_o, xs_r, outs_r
     nxt["rmsnorm_act_quant_T32768"] = rms
     # mask monitor over a bandwidth-sized input: the 16 gate masks of the
     # 2048/7168 stack, stacked row-wise (one flat bit stream), against the
