@@ -584,12 +584,13 @@ def test_gemv_grouped(sbl, T):
         assert_y_close(host(j["y"]), oracle.dequant(acc_ref, o["beta"], g))
 
 
-@pytest.mark.parametrize("T,n", [(1, 3), (4, 3), (16, 3), (1, 2)])
+@pytest.mark.parametrize("T,n", [(1, 3), (4, 3), (16, 3), (1, 2), (4, 2), (16, 2)])
 def test_gemv_grouped_full_sweep(sbl, T, n):
     """The decode sweep as the benchmark launches it: all 168 linears of the
     0.5B skeleton (24 layers x 7) in one grouped call, bf16 row scales, one
-    x~ per input width, at 3:4 and at 2:4; every int32 accumulator
-    (bit-exact) and every y against the oracle."""
+    x~ per input width, at 3:4 and at 2:4 and at every token count the
+    benchmark times; every int32 accumulator (bit-exact) and every y
+    against the oracle."""
     K_in = {"q": 896, "k": 896, "v": 896, "o": 896, "gate": 896, "up": 896, "down": 4864}
     xs = {}
     for K in (896, 4864):
