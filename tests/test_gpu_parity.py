@@ -193,6 +193,29 @@ def test_grouped_refresh(sbl):
 
 
 
+def test_grouped_refresh_wide_stack_as_benchmarked(sbl):
+    """The 2048/7168 stack's refresh as the benchmark launches it: all 112
+    latent matrices (16 layers x q, k, v, o, gate, up, down; 973M weights)
+    in one grouped 3:4 call with fp32 row scales and no mask output; the
+    packed codes and scales of a sample of matrices (each shape class, the
+    first and the last) compared in full with the oracle."""
+    jobs, keep = [], {}
+    sample = {(0, "q"), (0, "down"), (7, "gate"), (11, "v"), (15, "up"), (15, "down")}
+    for layer in range(synth.WIDE_LAYERS):
+        for name, N, K in synth.WIDE_LINEARS:
+            W = synth.latent_weight(f"gpu/widestack/L{layer}/{name}", N, K)
+            jobs.append(dict(W=dev(W), packed=torch.empty((N, K // 4), dtype=torch.uint8, device=DEV),
+                             scale=torch.empty(N, dtype=torch.float32, device=DEV)))
+            if (layer, name) in sample:
+                keep[len(jobs) - 1] = W
+    assert sum(j["W"].numel() for j in jobs) == 973078528
+    hostd, devd = sbl.refresh_descs(jobs)
+    sbl.nm_mask_quant_pack_grouped(hostd, devd, len(jobs), 3, 4, 0, DEV)
+    torch.cuda.synchronize()
+    for i, W in keep.items():
+        _check_quant(W, oracle.nm_mask(W, 3, 4), 0, jobs[i]["packed"], jobs[i]["scale"], None)
+
+
 @pytest.mark.parametrize("n,m,flags", [(3, 4, 0), (6, 8, 0), (3, 4, 1), (4, 8, 1), (2, 4, 1), (1, 4, 0)])
 def test_grouped_refresh_mixed_row_classes(sbl, n, m, flags):
     """One grouped call over rows of every footprint: short rows (a wave
