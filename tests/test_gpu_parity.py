@@ -369,8 +369,8 @@ def test_gemm_stores_stay_in_bounds(sbl, T, K, N):
 
 
 @pytest.mark.parametrize("name,N,K", [("q", 896, 896), ("k", 128, 896), ("gate", 4864, 896),
-                                      ("down", 896, 4864), ("wide_up", 7168, 2048),
-                                      ("wide_down", 2048, 7168)])
+                                      ("down", 896, 4864), ("wide_o", 2048, 2048),
+                                      ("wide_up", 7168, 2048), ("wide_down", 2048, 7168)])
 def test_full_size_layer(sbl, name, N, K):
     """Full-size prefill shapes (32768 tokens for the 0.5B skeleton, 8192 for
     the 2048/7168 stack), run end to end on the GPU; masks, codes, scales,
