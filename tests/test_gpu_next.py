@@ -290,3 +290,23 @@ def test_ste_backward_single_term_reductions_are_exact(sbl):
     # would move most results
     top = (dw_ref.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
     assert (top != dw_ref).mean() > 0.9
+
+
+def test_mask_stats_wide_gate_stack_as_benchmarked(sbl):
+    """The mask monitor at the size the benchmark times: the 16 gate masks of
+    the 2048/7168 stack stacked row-wise (114688 x 2048, 235M weights), the
+    masks of the latent weights against those after a small update; counts
+    equal to the oracle's over the same masks, the GPU masks equal to the
+    oracle's, and the packed-code validator clean on the stack's codes."""
+    rows, cols = 16 * 7168, 2048
+    W = synth.latent_weight("gpu/ms/wide/W", rows, cols)
+    W2 = W + synth.latent_weight("gpu/ms/wide/step", rows, cols, std=1e-4)
+    a = sbl.nm_mask_create(dev(W), 3, 4)
+    b = sbl.nm_mask_create(dev(W2), 3, 4)
+    ma, mb = oracle.nm_mask(W, 3, 4), oracle.nm_mask(W2, 3, 4)
+    assert np.array_equal(host(a), ma) and np.array_equal(host(b), mb)
+    got = host(sbl.nm_mask_stats(a, b, rows, cols, 3, 4))
+    ref = oracle.mask_stats(ma, mb, rows, cols, 3, 4)
+    assert tuple(int(v) for v in got) == ref and ref[1] == 0 and ref[0] > 0
+    _, packed, _, _ = sbl.nm_mask_quant_pack(dev(W), 3, 4, want_mask=False)
+    assert host(sbl.packed_codes_check(packed, 3, 4)).tolist() == [0, 0]
