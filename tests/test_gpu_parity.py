@@ -805,3 +805,34 @@ def test_repeat_runs_of_the_large_tile_kernels_are_bitwise_identical(sbl):
     assert torch.equal(yd1, yd2) and torch.equal(ad1, ad2)
     assert torch.equal(ys1, ys2) and torch.equal(as1, as2)
     assert torch.equal(yd1, ys1) and torch.equal(ad1, as1)
+
+
+@pytest.mark.parametrize("T,N", [(300, 260), (1, 70), (4, 70), (16, 33)])
+def test_widest_rows_the_boundary_accepts(sbl, T, N):
+    """K = 65536, the widest rows the boundary accepts: the fused mask +
+    quantise + pack, the activation quantiser and the product (the prefill
+    kernel for 300 tokens, the decode product for 1 to 16) against the
+    oracle, with accumulators up to 127 * 65536 in magnitude."""
+    K = 65536
+    W = synth.latent_weight(f"gpu/maxk/{T}x{N}/W", N, K)
+    x = synth.activations_bf16(f"gpu/maxk/{T}x{N}/x", T, K)
+    mask_d, packed_d, scale_d, sb_d = sbl.nm_mask_quant_pack(dev(W), 3, 4)
+    xq_d, beta_d = sbl.act_quant_i8(dev(x))
+    mask = oracle.nm_mask(W, 3, 4)
+    assert np.array_equal(host(mask_d), mask)
+    _check_quant(W, mask, 0, packed_d, scale_d, sb_d)
+    xq, beta = oracle.act_quant(x)
+    assert np.array_equal(host(xq_d), xq) and np.array_equal(host(beta_d), beta)
+    codes = oracle.ternary_codes(W, mask, oracle.row_scale(W)[0])
+    if T > 16:
+        y, acc = sbl.sparse_bitlinear_gemm(xq_d, beta_d, packed_d, scale_d, want_acc=True)
+    else:
+        y, acc = sbl.sparse_bitlinear_gemv(xq_d, beta_d, packed_d, scale_d, want_acc=True)
+    acc_ref = oracle.gemm_acc(xq, codes)
+    assert np.array_equal(host(acc), acc_ref)
+    assert_y_close(host(y), oracle.dequant(acc_ref, beta, oracle.row_scale(W)[0]))
+    # the same codes against all-127 activations: the largest sums
+    big = np.full((T, K), 127, np.int8)
+    yb, accb = (sbl.sparse_bitlinear_gemm if T > 16 else sbl.sparse_bitlinear_gemv)(
+        dev(big), dev(np.ones(T, np.float32)), packed_d, scale_d, want_acc=True)
+    assert np.array_equal(host(accb), oracle.gemm_acc(big, codes))
