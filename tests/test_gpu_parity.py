@@ -836,3 +836,34 @@ def test_widest_rows_the_boundary_accepts(sbl, T, N):
     yb, accb = (sbl.sparse_bitlinear_gemm if T > 16 else sbl.sparse_bitlinear_gemv)(
         dev(big), dev(np.ones(T, np.float32)), packed_d, scale_d, want_acc=True)
     assert np.array_equal(host(accb), oracle.gemm_acc(big, codes))
+
+
+def test_widest_rows_sparse24_and_ste(sbl):
+    """K = 65536 on the 2:4 path (compressor and smfmac product, acc equal to
+    the oracle's and y to the dense product's) and in the straight-through
+    backward (every entry within its bound)."""
+    T, N, K = 300, 260, 65536
+    o = _operands("gpu/maxk/sp24", T, K, N, n=2, m=4)
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sp = sbl.sparse24_compress(dev(o["packed"]), bad)
+    y, acc = sbl.sparse_bitlinear_gemm_sparse24(dev(o["xq"]), dev(o["beta"]), sp, N, dev(o["g"]),
+                                                want_acc=True)
+    yd = sbl.sparse_bitlinear_gemm(dev(o["xq"]), dev(o["beta"]), dev(o["packed"]), dev(o["g"]))[0]
+    assert int(bad.item()) == 0
+    assert np.array_equal(host(acc), oracle.gemm_acc(o["xq"], o["codes"]))
+    assert torch.equal(y, yd)
+    # backward: 64 tokens, 32 outputs, K = 65536 inputs
+    Ts, Ns = 64, 32
+    dy = synth.grad_output("gpu/maxk/ste/dy", Ts, Ns)
+    xq, beta, codes, g = o["xq"][:Ts], o["beta"][:Ts], o["codes"][:Ns], o["g"][:Ns]
+    dx, dw = sbl.sparse_bitlinear_ste_backward(dev(dy), dev(xq), dev(beta),
+                                               dev(oracle.pack_codes(codes)), dev(g))
+    dx_ref, dw_ref = oracle.ste_backward(dy, xq, beta, codes, g)
+    a = np.abs((dy * g[None, :]).astype(np.float32)).astype(np.float64)
+    s = (beta / np.float32(127)).astype(np.float32)
+    b = np.abs((dy * s[:, None]).astype(np.float32)).astype(np.float64)
+    u = 2.0 ** -24
+    bdx = (3 * Ns / 16 + 36) * u * (a @ np.abs(codes).astype(np.float64)) + 1e-37
+    bdw = (3 * Ts / 16 + 36) * u * (b.T @ np.abs(xq).astype(np.float64)) * g[:, None].astype(np.float64) + 1e-37
+    assert (np.abs(host(dx).astype(np.float64) - dx_ref) <= bdx).all()
+    assert (np.abs(host(dw).astype(np.float64) - dw_ref) <= bdw).all()
